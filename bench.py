@@ -1,0 +1,237 @@
+"""Benchmark of libpctree on one MI355X.
+
+One step = one pass of the whole hot path over one batch of the "b16"
+workload (batch 32, V = 151936, B = 16, k = 8, beam 16, N = 256, rank-256
+bf16 Markov factors): the parent-conditioned tree build (seed pre-pass, 16
+depths of fused Markov / log-sum-exp / top-k + per-request expand, global
+top-N), its packed ancestry mask, and the acceptance walk against synthetic
+target tokens (prepared before the timed region).  Inputs are resident in
+HBM before timing starts.
+
+Prints one JSON line (rank 0):
+  value        draft trees per second (whole job)
+  roofline     the fused Markov kernel at 512 parents per launch (depths 3..16)
+               against bf16 dense MFMA peak, durations from HIP events
+               recorded around its launches inside the timed region
+  cpu_baseline the CPU oracle on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-requests", type=int, default=2,
+                    help="requests of the workload timed on the CPU oracle")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-adaptive", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; "
+                          "--gpus must be 1"}), flush=True)
+        sys.exit(2)
+
+    import torch
+    import draft_tree_construction_markov_amd as pct
+    import synth
+
+    dev = torch.device("cuda:0")
+    w = synth.TREE_WORKLOADS["b16"]
+    t0 = time.time()
+    L, U, W, A = synth.tree_inputs(w)
+    log(f"inputs generated in {time.time() - t0:.1f}s")
+    dL = torch.from_numpy(L).to(dev)
+    dU, dW = pct.bf16_tensor(U, dev), pct.bf16_tensor(W, dev)
+    dA = torch.from_numpy(A).to(dev)
+    tb = pct.TreeBuilder(w.batch, w.B, w.V, w.k, w.beam_w, w.N, r=w.r,
+                         bf16=True, mask=True, device=dev)
+    out = tb.run(dL, dU, dW, dA)
+    torch.cuda.synchronize()
+    g = out.numpy()
+    tgt = synth.targets_from_tree(w.seed, g["tok"], g["parent"], g["depth"],
+                                  g["n_nodes"], A, w.V, w.B,
+                                  synth.round_agreement(w.B))
+    dT = torch.from_numpy(tgt).to(dev)
+    vout = (torch.empty(w.batch, dtype=torch.int32, device=dev),
+            torch.empty(w.batch, w.B, dtype=torch.int32, device=dev),
+            torch.empty(w.batch, w.B + 1, dtype=torch.int32, device=dev))
+
+    def step():
+        o = tb.run(dL, dU, dW, dA)
+        pct.verify_accept(o.tok, o.parent, o.depth, o.n_nodes, dT, w.B,
+                          out=vout)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region, with the per-launch events on
+    pct.profile_reset()
+    pct.profile_enable(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    pct.profile_enable(False)
+    ms_step = (t2 - t1) * 1e3 / args.steps
+    P_steady = w.batch * w.beam_w
+    k1_ms, k1_n = pct.profile_read(pct.PROF_MARKOV, P_steady)
+    k1_all_ms, k1_all_n = pct.profile_read(pct.PROF_MARKOV, -1)
+    kinds = {"markov": pct.PROF_MARKOV, "expand": pct.PROF_EXPAND,
+             "topn": pct.PROF_TOPN, "mask": pct.PROF_MASK,
+             "accept": pct.PROF_ACCEPT, "rowtop": pct.PROF_ROWTOP,
+             "init": pct.PROF_INIT}
+    per_kind = {}
+    for name, kd in kinds.items():
+        ms, n = pct.profile_read(kd, -1)
+        per_kind[name] = round(ms / args.steps, 4)
+    pct.profile_reset()
+
+    # same region without events, to show their overhead
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step_noev = (time.perf_counter() - t3) * 1e3 / args.steps
+
+    trees_s = w.batch / (ms_step / 1e3)
+    nodes_s = w.batch * w.N / (ms_step / 1e3)
+    tau = vout[0].cpu().numpy()
+
+    flop_per_parent = 2.0 * w.r * w.V
+    k1_avg_ms = k1_ms / max(k1_n, 1)
+    achieved = P_steady * flop_per_parent / (k1_avg_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1),
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": None,
+                "kernel": "markov_topk_mfma<2,8,16> (512 parents/launch)",
+                "avg_launch_ms": round(k1_avg_ms, 5),
+                "launches": k1_n}
+
+    res = {
+        "metric": "draft trees/sec & nodes/sec (V=151936,B=16,N=256,"
+                  "batch 32); % HBM/MFMA peak",
+        "value": round(trees_s, 1),
+        "unit": "trees/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16-mfma/fp32",
+        "data": "synthetic",
+        "config": {"workload": "b16: batch 32, V=151936, B=16, k=8, beam 16,"
+                               " N=256, r=256 bf16 Markov factors; build + "
+                               "mask + acceptance walk",
+                   "global_batch": w.batch, "parallelism": "none (1 GPU)"},
+        "nodes_per_sec": round(nodes_s, 1),
+        "ms_per_step_without_events": round(ms_step_noev, 4),
+        "kernel_ms_per_step": per_kind,
+        "markov_all_launches": {"ms_per_step": round(k1_all_ms / args.steps, 4),
+                                "launches_per_step": k1_all_n // args.steps},
+        "mean_tau": float(np.mean(tau)),
+        "roofline": roofline,
+    }
+
+    if not args.no_adaptive and hasattr(pct.lib(), "pct_build_tree_adaptive"):
+        res["adaptive"] = bench_adaptive(args, pct, synth, torch, dev)
+
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(args, w, L, U, W, A)
+    print(json.dumps(res), flush=True)
+
+
+def bench_adaptive(args, pct, synth, torch, dev):
+    a = synth.ADAPTIVE
+    t0 = time.time()
+    L, peaked, ctx = synth.adaptive_round(a["seed"], a["batch"], a["B"],
+                                          a["V"])
+    log(f"adaptive inputs in {time.time() - t0:.1f}s")
+    dL = torch.from_numpy(L).to(dev)
+    dC = torch.from_numpy(ctx).to(dev)
+    cost = {k: a[k] for k in ("C_d", "c0", "c1", "c2", "c_ell")}
+    ab = pct.AdaptiveBuilder(a["batch"], a["B"], a["V"], a["n_max"], cost,
+                             mask=True, device=dev)
+    for _ in range(args.warmup):
+        ab.run(dL, dC)
+    torch.cuda.synchronize()
+    pct.profile_reset()
+    pct.profile_enable(True)
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        ab.run(dL, dC)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t1) * 1e3 / args.steps
+    pct.profile_enable(False)
+    rs_ms, rs_n = pct.profile_read(pct.PROF_ROWSTATS, -1)
+    pct.profile_reset()
+    ns = ab.n_star.cpu().numpy()
+    bytes_rows = float(L.nbytes)
+    rs_avg = rs_ms / max(rs_n, 1)
+    gbs = bytes_rows / (rs_avg * 1e-3) / 1e9
+    return {"workload": "adaptive: batch 64, V=151936, B=16, n_max=1024, "
+                        "marginal rows, half peaked / half flat",
+            "trees_per_sec": round(a["batch"] / (ms / 1e3), 1),
+            "nodes_per_sec": round(float(ns.sum()) / (ms / 1e3), 1),
+            "ms_per_step": round(ms, 4),
+            "n_star_mean": float(ns.mean()), "n_star_std": float(ns.std()),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": None, "kernel": "row statistics",
+                         "avg_launch_ms": round(rs_avg, 5)}}
+
+
+def cpu_baseline(args, w, L, U, W, A):
+    import oracle
+    n = args.cpu_requests
+    t0 = time.perf_counter()
+    oracle.build_tree(L[:n], U, W, A[:n], w.k, w.beam_w, w.N)
+    el = time.perf_counter() - t0
+    return {"value": round(n / el, 4), "unit": "trees/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"first {n} requests of the b16 workload, tree build "
+                      f"only, single-threaded C oracle ({el:.1f}s) on "
+                      f"{cpu_model()}, nproc={os.cpu_count()}"}
+
+
+if __name__ == "__main__":
+    main()

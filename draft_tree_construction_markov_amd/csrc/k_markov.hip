@@ -1,0 +1,206 @@
+// k_markov.hip -- planning and dispatch of the fused Markov-logit kernel
+// (the MFMA kernel itself is in k_markov_impl.h), and its plain VALU variant.
+// The fused Markov-logit kernel of the parent-conditioned
+// tree (PCTree article, "chain -> tree": z_d(p) = L_d + Markov(p) for every
+// frontier parent in one batched call, then each parent's log-softmax and
+// local top-k).
+//
+// Markov(p)[v] = U[tok_p] . W[v] is a [P x r] x [r x V] contraction.  The
+// kernel computes it on bf16 MFMA (v_mfma_f32_32x32x16_bf16, fp32
+// accumulate) in 64-vocab tiles and consumes every logit in registers:
+//   z = L[row_p][v] + M[p][v]            (one fp32 add)
+//   running max / sum of 2^(z*log2e - c) per (lane, parent)  (log-sum-exp)
+//   candidates z >= theta_p kept in a per-(lane, parent) top-k list
+// The logit rows are never written back (unless z_out asks for them).
+//
+// Orientation: the MFMA "A" operand is the W tile (vocab rows), "B" is the
+// gathered U rows (parents), so every lane owns one parent column of a
+// 32x32 output block and 16 vocab rows of it: per-parent state lives in a
+// handful of registers.  Each wave keeps the U rows of its 64 (NB=2) or 32
+// (NB=1) parents resident in registers for the whole kernel; the W tile is
+// staged through LDS (double-buffered, XOR-swizzled 16-byte chunks) and
+// shared by all waves of the workgroup.  A workgroup covers one slice of the
+// vocabulary for up to NB*NW*32 parents; slices x parent tiles form the grid.
+#include "k_markov_impl.h"
+
+namespace pct {
+
+// Plain VALU variant for fp32 factors, ranks that are not a multiple of 16,
+// or no Markov term at all.  Grid: (vocab slice, parent); each thread walks
+// a strided part of the slice.
+template <int DT>  // 0 = fp32 factors, 1 = bf16 factors, 2 = none
+__global__ __launch_bounds__(kSimpleThreads) void markov_topk_simple(K1Args a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  ZV* lists = reinterpret_cast<ZV*>(smem);
+  __shared__ float red_c[kSimpleThreads / kWave];
+  __shared__ float red_s[kSimpleThreads / kWave];
+  const int tid = threadIdx.x;
+  const int slice = blockIdx.x, p = blockIdx.y;
+  const int v0 = slice * a.vslice, v1 = min(v0 + a.vslice, a.V);
+  const int tok = a.ptok ? min(max(a.ptok[p], 0), a.V - 1) : 0;
+  int64_t row = a.plrow ? a.plrow[p] : (int64_t)p * a.lrow_mul + a.lrow_add;
+  row = row < 0 ? 0 : (row >= a.L_rows ? a.L_rows - 1 : row);
+  const float* Lrow = a.L ? a.L + row * a.lstride : nullptr;
+  float thr = a.theta ? a.theta[p] : neg_inf();
+  float cm2 = neg_inf(), ss = 0.f;
+  int cnt = 0;
+  ZV* lst = lists + tid * a.k;
+  for (int v = v0 + tid; v < v1; v += kSimpleThreads) {
+    float mv = 0.f;
+    if (DT == 0) {
+      const float* u = reinterpret_cast<const float*>(a.U) + (int64_t)tok * a.r;
+      const float* w = reinterpret_cast<const float*>(a.W) + (int64_t)v * a.r;
+      for (int j = 0; j < a.r; ++j) mv = fmaf(u[j], w[j], mv);
+    } else if (DT == 1) {
+      const uint16_t* u =
+          reinterpret_cast<const uint16_t*>(a.U) + (int64_t)tok * a.r;
+      const uint16_t* w =
+          reinterpret_cast<const uint16_t*>(a.W) + (int64_t)v * a.r;
+      for (int j = 0; j < a.r; ++j)
+        mv = fmaf(bf16_bits_to_float(u[j]), bf16_bits_to_float(w[j]), mv);
+    }
+    const float z = (Lrow ? Lrow[v] : 0.f) + mv;
+    if (a.z_out) a.z_out[(int64_t)p * a.V + v] = z;
+    if (z >= thr) list_insert(lst, a.k, cnt, thr, z, v);
+    const float z2 = z * kLog2e;
+    if (z2 > cm2) {
+      ss *= __builtin_amdgcn_exp2f(cm2 - z2);
+      cm2 = z2;
+    }
+    ss += __builtin_amdgcn_exp2f(fmaf(z, kLog2e, -cm2));
+  }
+  // block reduction of (max, sum)
+  float m2 = wave_max(cm2);
+  float sc = (cm2 == neg_inf()) ? 0.f : ss * __builtin_amdgcn_exp2f(cm2 - m2);
+  sc = wave_sum(sc);
+  const int wv = tid / kWave;
+  if ((tid & 63) == 0) {
+    red_c[wv] = m2;
+    red_s[wv] = sc;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float M = red_c[0];
+    for (int i = 1; i < kSimpleThreads / kWave; ++i) M = fmaxf(M, red_c[i]);
+    float S = 0.f;
+    if (M != neg_inf())
+      for (int i = 0; i < kSimpleThreads / kWave; ++i)
+        if (red_c[i] != neg_inf())
+          S += red_s[i] * __builtin_amdgcn_exp2f(red_c[i] - M);
+    a.part_c[(int64_t)slice * a.P + p] = M;
+    a.part_s[(int64_t)slice * a.P + p] = S;
+  }
+  if (cnt > 0) {
+    int pos = atomicAdd(&a.gcnt[p], cnt);
+    for (int i = 0; i < cnt; ++i) {
+      a.gz[(int64_t)p * a.cap + pos + i] = lst[i].z;
+      a.gv[(int64_t)p * a.cap + pos + i] = lst[i].v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------
+// planning and launch
+
+static const int kCUs = 256;
+static const size_t kLdsPerCU = 160 * 1024 - 256;  // static LDS headroom
+
+K1Plan plan_k1(int P, int V, int r, int k, int uw_dtype, bool has_uw,
+               bool allow_mfma) {
+  K1Plan pl{};
+  const int R16 = r / 16;
+  const bool r_ok = allow_mfma && has_uw && uw_dtype == 1 && r % 16 == 0 &&
+                    (R16 == 2 || R16 == 4 || R16 == 8 || R16 == 16);
+  if (r_ok) {
+    pl.kind = K1_MFMA;
+    pl.R16 = R16;
+    if (P <= 32) {
+      pl.NB = 1;
+      pl.NW = 1;
+    } else if (P <= 256) {
+      pl.NB = 2;
+      pl.NW = 4;
+    } else {
+      pl.NB = 2;
+      pl.NW = 8;
+    }
+    const size_t wbytes = (size_t)2 * 64 * 2 * R16 * 16;
+    auto lds_of = [&](int nw) {
+      return wbytes + (size_t)nw * 64 * pl.NB * k * sizeof(ZV);
+    };
+    while (pl.NW > 1 && lds_of(pl.NW) > kLdsPerCU) pl.NW /= 2;
+    pl.lds = lds_of(pl.NW);
+    int per_cu = (int)(kLdsPerCU / pl.lds);
+    if (per_cu < 1) per_cu = 1;
+    const int by_waves = 8 / pl.NW > 0 ? 8 / pl.NW : 1;
+    if (per_cu > by_waves) per_cu = by_waves;
+    const int PT = (P + 32 * pl.NB * pl.NW - 1) / (32 * pl.NB * pl.NW);
+    pl.n_tiles = (V + 63) / 64;
+    int target = kCUs * per_cu;
+    int S = (target + PT - 1) / PT;
+    if (S > pl.n_tiles) S = pl.n_tiles;
+    if (S < 1) S = 1;
+    pl.tiles_per_slice = (pl.n_tiles + S - 1) / S;
+    pl.n_slices = (pl.n_tiles + pl.tiles_per_slice - 1) / pl.tiles_per_slice;
+    pl.cap = pl.n_slices * 2 * k;
+    pl.grid = dim3(pl.n_slices, PT);
+    pl.block = dim3(pl.NW * 64);
+  } else {
+    pl.kind = K1_SIMPLE;
+    pl.R16 = 0;
+    int S = (2048 + P - 1) / P;
+    const int max_s = (V + kSimpleThreads - 1) / kSimpleThreads;
+    if (S > max_s) S = max_s;
+    if (S < 1) S = 1;
+    pl.vslice = (V + S - 1) / S;
+    pl.n_slices = (V + pl.vslice - 1) / pl.vslice;
+    pl.cap = pl.n_slices * kSimpleThreads * k;
+    pl.lds = (size_t)kSimpleThreads * k * sizeof(ZV);
+    pl.grid = dim3(pl.n_slices, P);
+    pl.block = dim3(kSimpleThreads);
+  }
+  return pl;
+}
+
+hipError_t launch_mfma_r2(const K1Plan&, const K1Args&, hipStream_t);
+hipError_t launch_mfma_r4(const K1Plan&, const K1Args&, hipStream_t);
+hipError_t launch_mfma_r8(const K1Plan&, const K1Args&, hipStream_t);
+hipError_t launch_mfma_r16(const K1Plan&, const K1Args&, hipStream_t);
+
+template <int DT>
+static hipError_t go_simple(const K1Plan& pl, const K1Args& a,
+                            hipStream_t s) {
+  auto fn = markov_topk_simple<DT>;
+  hipError_t e = allow_lds(reinterpret_cast<const void*>(fn), pl.lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fn, pl.grid, pl.block, pl.lds, s, a);
+  return hipGetLastError();
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int n, int32_t v) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s) {
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, s,
+                     p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_k1(const K1Plan& pl, const K1Args& a, hipStream_t s) {
+  if (pl.kind == K1_MFMA) {
+    switch (pl.R16) {
+      case 2: return launch_mfma_r2(pl, a, s);
+      case 4: return launch_mfma_r4(pl, a, s);
+      case 8: return launch_mfma_r8(pl, a, s);
+      case 16: return launch_mfma_r16(pl, a, s);
+    }
+    return hipErrorInvalidValue;
+  }
+  if (a.U == nullptr) return go_simple<2>(pl, a, s);
+  if (a.dt == 1) return go_simple<1>(pl, a, s);
+  return go_simple<0>(pl, a, s);
+}
+
+}  // namespace pct

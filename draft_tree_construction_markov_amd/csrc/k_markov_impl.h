@@ -1,0 +1,305 @@
+// k_markov_impl.h -- the fused Markov-logit kernel of the parent-conditioned
+// tree (PCTree article, "chain -> tree": z_d(p) = L_d + Markov(p) for every
+// frontier parent in one batched call, then each parent's log-softmax and
+// local top-k).
+//
+// Markov(p)[v] = U[tok_p] . W[v] is a [P x r] x [r x V] contraction.  The
+// kernel computes it on bf16 MFMA (v_mfma_f32_32x32x16_bf16, fp32
+// accumulate) in 64-vocab tiles and consumes every logit in registers:
+//   z = L[row_p][v] + M[p][v]            (one fp32 add)
+//   running max / sum of 2^(z*log2e - c) per (lane, parent)  (log-sum-exp)
+//   candidates z >= theta_p kept in a per-(lane, parent) top-k list
+// The logit rows are never written back (unless z_out asks for them).
+//
+// Orientation: the MFMA "A" operand is the W tile (vocab rows), "B" is the
+// gathered U rows (parents), so every lane owns one parent column of a
+// 32x32 output block and 16 vocab rows of it: per-parent state lives in a
+// handful of registers.  Each wave keeps the U rows of its 64 (NB=2) or 32
+// (NB=1) parents resident in registers for the whole kernel; the W tile is
+// staged through LDS by direct global->LDS loads (double-buffered,
+// XOR-swizzled 16-byte chunks) and
+// shared by all waves of the workgroup.  A workgroup covers one slice of the
+// vocabulary for up to NB*NW*32 parents; slices x parent tiles form the grid.
+#pragma once
+#include "pct_device.h"
+#include "pct_internal.h"
+
+namespace pct {
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef const __attribute__((address_space(1))) void* gbl_ptr_t;
+
+template <int R16>
+__device__ __forceinline__ int wswz(int row, int c) {
+  return row * (2 * R16) + (c ^ (row & (2 * R16 - 1)));
+}
+
+// Insert z (vocab v) into a lane's top-k list.  Within one lane the vocab
+// index only grows, so an entry equal to the current minimum never wins.
+__device__ __forceinline__ void list_insert(ZV* lst, int k, int& cnt,
+                                            float& thr, float z, int v) {
+  if (cnt < k) {
+    lst[cnt] = ZV{z, v};
+    ++cnt;
+    if (cnt == k) {
+      float mn = lst[0].z;
+      for (int i = 1; i < k; ++i) mn = fminf(mn, lst[i].z);
+      thr = mn;
+    }
+  } else if (z > thr) {
+    int wi = 0;
+    float wz = lst[0].z;
+    int wv = lst[0].v;
+    for (int i = 1; i < k; ++i) {
+      ZV e = lst[i];
+      if (e.z < wz || (e.z == wz && e.v > wv)) {
+        wi = i;
+        wz = e.z;
+        wv = e.v;
+      }
+    }
+    lst[wi] = ZV{z, v};
+    float mn = lst[0].z;
+    for (int i = 1; i < k; ++i) mn = fminf(mn, lst[i].z);
+    thr = mn;
+  }
+}
+
+__device__ __forceinline__ void flush_lane(const K1Args& a, int p, int slice,
+                                           float c2, float s, ZV* lst,
+                                           int cnt, bool writer) {
+  if (writer) {
+    a.part_c[(int64_t)slice * a.P + p] = c2;
+    a.part_s[(int64_t)slice * a.P + p] = s;
+  }
+  if (cnt > 0) {
+    int pos = atomicAdd(&a.gcnt[p], cnt);
+    float* gz = a.gz + (int64_t)p * a.cap + pos;
+    int32_t* gv = a.gv + (int64_t)p * a.cap + pos;
+    for (int i = 0; i < cnt; ++i) {
+      gz[i] = lst[i].z;
+      gv[i] = lst[i].v;
+    }
+  }
+}
+
+// Combine the (max, sum) partials of lanes l and l^32 (same parent).
+__device__ __forceinline__ void combine_halves(float& c2, float& s) {
+  float oc2 = __shfl_xor(c2, 32, kWave);
+  float os = __shfl_xor(s, 32, kWave);
+  float m2 = fmaxf(c2, oc2);
+  float r = 0.f;
+  if (m2 != neg_inf()) {
+    if (c2 != neg_inf()) r += s * __builtin_amdgcn_exp2f(c2 - m2);
+    if (oc2 != neg_inf()) r += os * __builtin_amdgcn_exp2f(oc2 - m2);
+  }
+  c2 = m2;
+  s = r;
+}
+
+template <int NB, int NW, int R16>
+__global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
+  constexpr int NT = NW * 64;
+  constexpr int CH = 2 * R16;               // 16-byte chunks per W row
+  constexpr int TILE_CH = 64 * CH;          // chunks per 64-row tile
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint4* wlds = reinterpret_cast<uint4*>(smem);  // [2][TILE_CH]
+  ZV* lists = reinterpret_cast<ZV*>(smem + 2 * TILE_CH * 16);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, col = lane & 31;
+  const int slice = blockIdx.x;
+  const int t0 = slice * a.tiles_per_slice;
+  const int t1 = min(t0 + a.tiles_per_slice, a.n_tiles);
+  const int pw = blockIdx.y * (NW * NB * 32) + wave * (NB * 32);
+  const bool has_L = a.L != nullptr;
+  const uint4* Wg = reinterpret_cast<const uint4*>(a.W);
+
+  bf16x8 uf[NB][R16];
+  const float* lrow[NB];
+  float thr[NB], cm2[NB], ss[NB];
+  int cnt[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int p = pw + 32 * b + col;
+    const bool valid = p < a.P;
+    const int pc = valid ? p : a.P - 1;
+    const int tok = min(max(a.ptok[pc], 0), a.V - 1);
+    int64_t row =
+        a.plrow ? a.plrow[pc] : (int64_t)pc * a.lrow_mul + a.lrow_add;
+    row = row < 0 ? 0 : (row >= a.L_rows ? a.L_rows - 1 : row);
+    lrow[b] = has_L ? a.L + row * a.lstride : nullptr;
+    const uint4* up =
+        reinterpret_cast<const uint4*>(a.U) + (int64_t)tok * CH + h;
+#pragma unroll
+    for (int kk = 0; kk < R16; ++kk) {
+      uint4 raw = up[2 * kk];
+      if (!valid) raw = make_uint4(0, 0, 0, 0);
+      uf[b][kk] = __builtin_bit_cast(bf16x8, raw);
+    }
+    thr[b] = valid ? (a.theta ? a.theta[p] : neg_inf()) : pos_inf();
+    cm2[b] = neg_inf();
+    ss[b] = 0.f;
+    cnt[b] = 0;
+  }
+
+  // W tile t -> LDS buffer buf by direct global->LDS loads: each wave
+  // instruction fills 64 consecutive 16-byte slots; slot q holds row q/CH,
+  // logical chunk (q%CH) ^ (row & (CH-1)).  Rows past V are clamped to row
+  // V-1 (their outputs are masked in the epilogue).
+  auto issue_tile = [&](int t, int buf) {
+#pragma unroll
+    for (int gi = wave; gi < TILE_CH / 64; gi += NW) {
+      const int q = gi * 64 + lane;
+      const int row = q / CH;
+      const int c = (q % CH) ^ (row & (CH - 1));
+      const int v = min(64 * t + row, a.V - 1);
+      __builtin_amdgcn_global_load_lds(
+          (gbl_ptr_t)(Wg + (int64_t)v * CH + c),
+          (lds_ptr_t)(wlds + buf * TILE_CH + gi * 64), 16, 0, 0);
+    }
+  };
+
+  if (t0 < t1) issue_tile(t0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  for (int t = t0; t < t1; ++t) {
+    const int buf = (t - t0) & 1;
+    if (t + 1 < t1) issue_tile(t + 1, buf ^ 1);
+    const uint4* wt = wlds + buf * TILE_CH;
+    const bool full = 64 * t + 64 <= a.V;
+#pragma unroll
+    for (int av = 0; av < 2; ++av) {
+      f32x16 acc[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[b][j] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < R16; ++kk) {
+        const bf16x8 wf =
+            __builtin_bit_cast(bf16x8, wt[wswz<R16>(32 * av + col, 2 * kk + h)]);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, uf[b][kk],
+                                                          acc[b], 0, 0, 0);
+      }
+      // register j of this lane holds vocab vb + 8*(j/4) + j%4
+      const int vb = 64 * t + 32 * av + 4 * h;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        float z[16];
+        if (full && a.vec_ok) {
+          if (has_L) {
+            const float4* lp = reinterpret_cast<const float4*>(lrow[b] + vb);
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const float4 l4 = lp[2 * g];
+              z[4 * g + 0] = l4.x + acc[b][4 * g + 0];
+              z[4 * g + 1] = l4.y + acc[b][4 * g + 1];
+              z[4 * g + 2] = l4.z + acc[b][4 * g + 2];
+              z[4 * g + 3] = l4.w + acc[b][4 * g + 3];
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) z[j] = acc[b][j];
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int v = vb + 8 * (j >> 2) + (j & 3);
+            const float l = (has_L && v < a.V) ? lrow[b][v] : 0.f;
+            z[j] = v < a.V ? l + acc[b][j] : neg_inf();
+          }
+        }
+        float m = z[0];
+#pragma unroll
+        for (int j = 1; j < 16; ++j) m = fmaxf(m, z[j]);
+
+        const int p = pw + 32 * b + col;
+        if (a.z_out != nullptr && p < a.P) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int v = vb + 8 * (j >> 2) + (j & 3);
+            if (v < a.V) a.z_out[(int64_t)p * a.V + v] = z[j];
+          }
+        }
+        // online log-sum-exp in log2 units
+        const float m2 = m * kLog2e;
+        if (m2 > cm2[b]) {
+          ss[b] *= __builtin_amdgcn_exp2f(cm2[b] - m2);
+          cm2[b] = m2;
+        }
+        if (m != neg_inf()) {
+          float sg[4];
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float e0 = __builtin_amdgcn_exp2f(fmaf(z[4 * g], kLog2e, -cm2[b]));
+            const float e1 = __builtin_amdgcn_exp2f(fmaf(z[4 * g + 1], kLog2e, -cm2[b]));
+            const float e2 = __builtin_amdgcn_exp2f(fmaf(z[4 * g + 2], kLog2e, -cm2[b]));
+            const float e3 = __builtin_amdgcn_exp2f(fmaf(z[4 * g + 3], kLog2e, -cm2[b]));
+            sg[g] = (e0 + e1) + (e2 + e3);
+          }
+          ss[b] += (sg[0] + sg[1]) + (sg[2] + sg[3]);
+        }
+        // rare path: some element may enter this lane's top-k.  A rolled
+        // loop that shifts z keeps the code small; z is dead afterwards.
+        const bool hit = m >= thr[b];
+        if (__any(hit)) {
+          if (hit) {
+            ZV* lst = lists + ((wave * 64 + lane) * NB + b) * a.k;
+            int v = vb;
+#pragma unroll 1
+            for (int j = 0; j < 16; ++j) {
+              const float zj = z[0];
+#pragma unroll
+              for (int i = 0; i < 15; ++i) z[i] = z[i + 1];
+              if (zj >= thr[b] && v < a.V)
+                list_insert(lst, a.k, cnt[b], thr[b], zj, v);
+              v += ((j & 3) == 3) ? 5 : 1;
+            }
+          }
+        }
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    float c2 = cm2[b], s = ss[b];
+    combine_halves(c2, s);
+    const int p = pw + 32 * b + col;
+    if (p < a.P) {
+      ZV* lst = lists + ((wave * 64 + lane) * NB + b) * a.k;
+      flush_lane(a, p, slice, c2, s, lst, cnt[b], h == 0);
+    }
+  }
+}
+
+
+template <int NB, int NW, int R16>
+hipError_t go_mfma(const K1Plan& pl, const K1Args& a, hipStream_t s) {
+  auto fn = markov_topk_mfma<NB, NW, R16>;
+  hipError_t e = allow_lds(reinterpret_cast<const void*>(fn), pl.lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fn, pl.grid, pl.block, pl.lds, s, a);
+  return hipGetLastError();
+}
+
+// Launcher for one rank (r = 16*R16): picks the (NB, NW) instantiation.
+template <int R16>
+hipError_t launch_mfma_rank(const K1Plan& pl, const K1Args& a,
+                            hipStream_t s) {
+  if (pl.NB == 1) return go_mfma<1, 1, R16>(pl, a, s);
+  switch (pl.NW) {
+    case 8: return go_mfma<2, 8, R16>(pl, a, s);
+    case 4: return go_mfma<2, 4, R16>(pl, a, s);
+    case 2: return go_mfma<2, 2, R16>(pl, a, s);
+    default: return go_mfma<2, 1, R16>(pl, a, s);
+  }
+}
+
+}  // namespace pct

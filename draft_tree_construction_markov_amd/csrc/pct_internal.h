@@ -1,0 +1,163 @@
+// pct_internal.h -- host-side plumbing shared by the libpctree translation
+// units: kernel argument blocks, launch plans and launcher declarations.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pct {
+
+// Candidate-list entry of the fused Markov kernel.
+struct ZV {
+  float z;
+  int32_t v;
+};
+
+// Arguments of the fused Markov / log-sum-exp / top-k kernels.
+struct K1Args {
+  const float* L;      // logits rows (may be null: z = Markov only)
+  int64_t lstride;     // elements between L rows
+  int vec_ok;          // rows 16-byte aligned: vector loads allowed
+  const void* U;       // [V][r] factors (null: z = L)
+  const void* W;       // [V][r], vocab-major
+  int dt;              // factor element type: 0 fp32, 1 bf16
+  int V, r, P, k;
+  const int32_t* ptok;   // [P] parent tokens
+  const int32_t* plrow;  // [P] L row of each parent (null: p*lrow_mul+lrow_add)
+  int lrow_mul, lrow_add;
+  int64_t L_rows;        // rows of L (row indices are clamped to it)
+  const float* theta;    // [P] candidate threshold seeds (null: -inf)
+  int tiles_per_slice, n_tiles, n_slices;  // mfma: 64-vocab tiles
+  int vslice;                              // simple: vocab per slice
+  float* part_c;   // [n_slices][P] running max in log2 units
+  float* part_s;   // [n_slices][P] sum of 2^(z*log2e - part_c)
+  int32_t* gcnt;   // [P] candidates per parent (zeroed before launch)
+  float* gz;       // [P][cap]
+  int32_t* gv;     // [P][cap]
+  int cap;
+  float* z_out;    // [P][V] optional
+};
+
+enum K1Kind { K1_MFMA = 0, K1_SIMPLE = 1 };
+
+struct K1Plan {
+  int kind;
+  int NB, NW, R16;
+  int n_tiles, tiles_per_slice, n_slices, vslice;
+  int cap;  // candidate capacity per parent
+  size_t lds;
+  dim3 grid, block;
+};
+
+constexpr int kSeedT = 32;         // top tokens of each L row used for seeds
+constexpr int kSimpleThreads = 128;
+constexpr int kMaxPool = 8192;     // generated children per request
+constexpr int kMaxCand = 2048;     // children per request and depth
+constexpr int kMaxK = 64;
+
+// Allow a kernel more than the default 64 KB of dynamic LDS; only called
+// when a launch needs it.  A failure is consumed (not left as the thread's
+// last error) and returned.
+inline hipError_t allow_lds(const void* fn, size_t bytes) {
+  if (bytes <= 64 * 1024) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute(
+      fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e != hipSuccess) (void)hipGetLastError();
+  return e;
+}
+
+// Kernel kinds reported by the profiler (see pct_profile_read).
+enum ProfKind {
+  PROF_MARKOV = 0,   // fused Markov / log-sum-exp / top-k kernel
+  PROF_EXPAND = 1,   // per-request merge, scores and beam
+  PROF_TOPN = 2,     // global top-N
+  PROF_MASK = 3,     // ancestry mask
+  PROF_ACCEPT = 4,   // acceptance walk
+  PROF_ROWTOP = 5,   // seed pre-pass over the logit rows
+  PROF_INIT = 6,     // depth-1 frontier
+  PROF_ROWSTATS = 7, // adaptive: streaming log-softmax + select
+  PROF_BESTFIRST = 8,// adaptive: best-first order + stop
+  PROF_FINALIZE = 9  // standalone Markov call: per-parent results
+};
+
+// RAII bracket of one launch (no-op unless profiling is enabled).
+class ProfScope {
+ public:
+  ProfScope(int kind, int64_t units, hipStream_t s);
+  ~ProfScope();
+
+ private:
+  hipStream_t stream_;
+  int idx_;
+};
+
+K1Plan plan_k1(int P, int V, int r, int k, int uw_dtype, bool has_uw,
+               bool allow_mfma = true);
+hipError_t launch_k1(const K1Plan& pl, const K1Args& a, hipStream_t s);
+
+// Per-request state of the depth loop.
+struct Frontier {
+  int32_t* tok;
+  int32_t* pid;
+  int32_t* lrow;
+  float* s;
+  float* theta;
+};
+
+struct SeedArgs {
+  const float* L;
+  int64_t lstride;
+  const int32_t* rowtop;  // [rows][kSeedT]
+  const void* U;
+  const void* W;
+  int uw_bf16, r, V, k;
+  int use_seed;
+};
+
+struct ExpandArgs {
+  int d, B, Fp, Fn, k, N, batch;
+  int base_d, pool_n;
+  int shared_stats;  // all parents of a request share one statistics row
+  int n_slices, Pstat, cap;
+  const float* part_c;
+  const float* part_s;
+  const int32_t* gcnt;
+  const float* gz;
+  const int32_t* gv;
+  Frontier cur, nxt;
+  int32_t* gcnt_next;  // zeroed for the next depth's parents
+  uint64_t* pool_key;  // [batch][pool_n]
+  SeedArgs seed;
+};
+
+struct TopNArgs {
+  int batch, B, N, pool_n;
+  int base[66];  // pool id where depth d starts (d = 1..B), base[B+1] = end
+  const uint64_t* pool_key;
+  int32_t *tok, *parent, *depth;
+  float* score;
+  int32_t* n_nodes;
+};
+
+hipError_t launch_rowtop(const float* L, int rows, int V, int64_t lstride,
+                         int vec_ok, int32_t* rowtop, hipStream_t s);
+hipError_t launch_init(int batch, int B, const int32_t* anchor, Frontier f,
+                       int32_t* gcnt, const SeedArgs& sa, hipStream_t s);
+hipError_t launch_expand(const ExpandArgs& a, hipStream_t s);
+hipError_t launch_topn(const TopNArgs& a, hipStream_t s);
+hipError_t launch_finalize(int P, int k, int n_slices, const float* part_c,
+                           const float* part_s, const int32_t* gcnt,
+                           const float* gz, const int32_t* gv, int cap,
+                           float* lse, int32_t* topk_tok, float* topk_logp,
+                           hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
+hipError_t launch_mask(int batch, int N, const int32_t* parent,
+                       const int32_t* n_nodes, uint64_t* mask, hipStream_t s);
+hipError_t launch_accept(int batch, int N, int B, const int32_t* tok,
+                         const int32_t* parent, const int32_t* depth,
+                         const int32_t* n_nodes, const int32_t* target,
+                         int32_t* tau, int32_t* accept_node,
+                         int32_t* accept_tok, hipStream_t s);
+
+}  // namespace pct
