@@ -46,6 +46,9 @@ def parse():
                     help="requests of the workload timed on the CPU oracle")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-adaptive", action="store_true")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="run a plain device copy of this size first "
+                         "(traffic-counter calibration)")
     return ap.parse_args()
 
 
@@ -100,17 +103,34 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # timed region, with the per-launch events on
-    pct.profile_reset()
-    pct.profile_enable(True)
+    if args.calib_copy_mb:
+        # a plain device copy of known size, for scaling traffic counters
+        n = args.calib_copy_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # timed region: K steps, inputs resident, no instrumentation
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
-    t2 = time.perf_counter()
+    ms_step = (time.perf_counter() - t1) * 1e3 / args.steps
+
+    # the same K steps again with HIP events around every launch (on the
+    # launch stream, recorded by the library) for per-kernel durations
+    pct.profile_reset()
+    pct.profile_enable(True)
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step_ev = (time.perf_counter() - t3) * 1e3 / args.steps
     pct.profile_enable(False)
-    ms_step = (t2 - t1) * 1e3 / args.steps
     P_steady = w.batch * w.beam_w
     k1_ms, k1_n = pct.profile_read(pct.PROF_MARKOV, P_steady)
     k1_all_ms, k1_all_n = pct.profile_read(pct.PROF_MARKOV, -1)
@@ -123,14 +143,6 @@ def main():
         ms, n = pct.profile_read(kd, -1)
         per_kind[name] = round(ms / args.steps, 4)
     pct.profile_reset()
-
-    # same region without events, to show their overhead
-    torch.cuda.synchronize()
-    t3 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    ms_step_noev = (time.perf_counter() - t3) * 1e3 / args.steps
 
     trees_s = w.batch / (ms_step / 1e3)
     nodes_s = w.batch * w.N / (ms_step / 1e3)
@@ -163,7 +175,7 @@ def main():
                                "mask + acceptance walk",
                    "global_batch": w.batch, "parallelism": "none (1 GPU)"},
         "nodes_per_sec": round(nodes_s, 1),
-        "ms_per_step_without_events": round(ms_step_noev, 4),
+        "ms_per_step_with_events": round(ms_step_ev, 4),
         "kernel_ms_per_step": per_kind,
         "markov_all_launches": {"ms_per_step": round(k1_all_ms / args.steps, 4),
                                 "launches_per_step": k1_all_n // args.steps},

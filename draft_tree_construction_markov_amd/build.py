@@ -12,8 +12,10 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpctree.so")
-SOURCES = ["api.hip", "k_markov.hip", "k_markov_r2.hip", "k_markov_r4.hip",
-           "k_markov_r8.hip", "k_markov_r16.hip", "k_select.hip",
+SOURCES = ["api.hip", "k_markov.hip",
+           "k_markov_r2s.hip", "k_markov_r2d.hip", "k_markov_r4s.hip",
+           "k_markov_r4d.hip", "k_markov_r8s.hip", "k_markov_r8d.hip",
+           "k_markov_r16s.hip", "k_markov_r16d.hip", "k_select.hip",
            "k_verify.hip", "k_adaptive.hip", "profile.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -94,7 +94,8 @@ pct_status plan_tree(const pct_tree_shape* sh, TreePlan& tp) {
   for (int d = 1; d <= B; ++d) {
     // without Markov factors every parent of a request shares its row
     const int P = has_uw ? sh->batch * tp.F[d - 1] : sh->batch;
-    tp.k1[d] = plan_k1(P, sh->V, sh->r, sh->k, sh->uw_dtype, has_uw);
+    tp.k1[d] = plan_k1(P, sh->V, sh->r, sh->k, sh->uw_dtype, has_uw, true,
+                       has_uw ? tp.F[d - 1] : 0);
     const int sp = tp.k1[d].n_slices * P;
     const int cp = tp.k1[d].cap * P;
     if (sp > tp.max_slices_P) tp.max_slices_P = sp;
@@ -351,7 +352,12 @@ pct_status pct_build_tree(const pct_tree_shape* shape, const float* L,
     a.k = sh.k;
     if (has_uw) {
       a.ptok = cur.tok;
-      a.plrow = cur.lrow;
+      // parent q*Fp + j reads row q*B + d-1: grouped rows
+      a.plrow = nullptr;
+      a.lrow_mul = B;
+      a.lrow_add = d - 1;
+      a.group_fp = Fp;
+      a.lslots = vec_ok ? pl.lslots : 0;
       a.theta = sa.use_seed ? cur.theta : nullptr;
     } else {
       // no Markov term: every parent of request q shares row q*B + d-1, so

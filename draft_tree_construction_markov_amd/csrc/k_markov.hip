@@ -38,7 +38,10 @@ __global__ __launch_bounds__(kSimpleThreads) void markov_topk_simple(K1Args a) {
   const int slice = blockIdx.x, p = blockIdx.y;
   const int v0 = slice * a.vslice, v1 = min(v0 + a.vslice, a.V);
   const int tok = a.ptok ? min(max(a.ptok[p], 0), a.V - 1) : 0;
-  int64_t row = a.plrow ? a.plrow[p] : (int64_t)p * a.lrow_mul + a.lrow_add;
+  int64_t row = a.plrow ? a.plrow[p]
+                        : (int64_t)(a.group_fp > 0 ? p / a.group_fp : p) *
+                                  a.lrow_mul +
+                              a.lrow_add;
   row = row < 0 ? 0 : (row >= a.L_rows ? a.L_rows - 1 : row);
   const float* Lrow = a.L ? a.L + row * a.lstride : nullptr;
   float thr = a.theta ? a.theta[p] : neg_inf();
@@ -106,7 +109,7 @@ static const int kCUs = 256;
 static const size_t kLdsPerCU = 160 * 1024 - 256;  // static LDS headroom
 
 K1Plan plan_k1(int P, int V, int r, int k, int uw_dtype, bool has_uw,
-               bool allow_mfma) {
+               bool allow_mfma, int group_fp) {
   K1Plan pl{};
   const int R16 = r / 16;
   const bool r_ok = allow_mfma && has_uw && uw_dtype == 1 && r % 16 == 0 &&
@@ -124,13 +127,39 @@ K1Plan plan_k1(int P, int V, int r, int k, int uw_dtype, bool has_uw,
       pl.NB = 2;
       pl.NW = 8;
     }
+    // static LDS: two W tiles and two L row buffers; dynamic: the lists
     const size_t wbytes = (size_t)2 * 64 * 2 * R16 * 16;
-    auto lds_of = [&](int nw) {
-      return wbytes + (size_t)nw * 64 * pl.NB * k * sizeof(ZV);
+    auto slots_of = [&](int nw) {
+      if (group_fp <= 0) return 0;
+      const int span = nw * pl.NB * 32;
+      return (span + group_fp - 1) / group_fp + 1;
     };
-    while (pl.NW > 1 && lds_of(pl.NW) > kLdsPerCU) pl.NW /= 2;
-    pl.lds = lds_of(pl.NW);
-    int per_cu = (int)(kLdsPerCU / pl.lds);
+    auto lists_of = [&](int nw) {  // lists + their lengths
+      return (size_t)nw * 64 * pl.NB * (k * sizeof(ZV) + sizeof(int));
+    };
+    const size_t staged_l = (size_t)2 * kLdsRowSlots * 16 * 16;
+    const size_t direct_l = (size_t)2 * 4 * 16 * 16;
+    // staged L rows when they fit kLdsRowSlots, shrinking the workgroup if
+    // needed; otherwise rows are read directly
+    int nw = pl.NW;
+    while (nw > 1 && (slots_of(nw) > kLdsRowSlots ||
+                      wbytes + staged_l + lists_of(nw) > kLdsPerCU))
+      nw /= 2;
+    if (group_fp > 0 && slots_of(nw) <= kLdsRowSlots &&
+        wbytes + staged_l + lists_of(nw) <= kLdsPerCU && nw >= 1) {
+      pl.NW = nw;
+      pl.lslots = kLdsRowSlots;
+      pl.lds = lists_of(nw);
+      pl.lds_total = wbytes + staged_l + pl.lds;
+    } else {
+      while (pl.NW > 1 && wbytes + direct_l + lists_of(pl.NW) > kLdsPerCU)
+        pl.NW /= 2;
+      pl.lslots = 0;
+      pl.lds = lists_of(pl.NW);
+      pl.lds_total = wbytes + direct_l + pl.lds;
+    }
+    if (pl.NB == 1 && pl.NW != 1) pl.NW = 1;
+    int per_cu = (int)(kLdsPerCU / pl.lds_total);
     if (per_cu < 1) per_cu = 1;
     const int by_waves = 8 / pl.NW > 0 ? 8 / pl.NW : 1;
     if (per_cu > by_waves) per_cu = by_waves;
@@ -162,10 +191,14 @@ K1Plan plan_k1(int P, int V, int r, int k, int uw_dtype, bool has_uw,
   return pl;
 }
 
-hipError_t launch_mfma_r2(const K1Plan&, const K1Args&, hipStream_t);
-hipError_t launch_mfma_r4(const K1Plan&, const K1Args&, hipStream_t);
-hipError_t launch_mfma_r8(const K1Plan&, const K1Args&, hipStream_t);
-hipError_t launch_mfma_r16(const K1Plan&, const K1Args&, hipStream_t);
+#define PCT_DECL_RANK(R)                                                  \
+  hipError_t launch_mfma_r##R##s(const K1Plan&, const K1Args&, hipStream_t); \
+  hipError_t launch_mfma_r##R##d(const K1Plan&, const K1Args&, hipStream_t);
+PCT_DECL_RANK(2)
+PCT_DECL_RANK(4)
+PCT_DECL_RANK(8)
+PCT_DECL_RANK(16)
+#undef PCT_DECL_RANK
 
 template <int DT>
 static hipError_t go_simple(const K1Plan& pl, const K1Args& a,
@@ -190,11 +223,14 @@ hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s) {
 
 hipError_t launch_k1(const K1Plan& pl, const K1Args& a, hipStream_t s) {
   if (pl.kind == K1_MFMA) {
+    const bool st = a.group_fp > 0 && a.lslots > 0 && a.vec_ok &&
+                    a.L != nullptr && a.plrow == nullptr;
     switch (pl.R16) {
-      case 2: return launch_mfma_r2(pl, a, s);
-      case 4: return launch_mfma_r4(pl, a, s);
-      case 8: return launch_mfma_r8(pl, a, s);
-      case 16: return launch_mfma_r16(pl, a, s);
+      case 2: return st ? launch_mfma_r2s(pl, a, s) : launch_mfma_r2d(pl, a, s);
+      case 4: return st ? launch_mfma_r4s(pl, a, s) : launch_mfma_r4d(pl, a, s);
+      case 8: return st ? launch_mfma_r8s(pl, a, s) : launch_mfma_r8d(pl, a, s);
+      case 16:
+        return st ? launch_mfma_r16s(pl, a, s) : launch_mfma_r16d(pl, a, s);
     }
     return hipErrorInvalidValue;
   }

@@ -17,8 +17,8 @@
 // handful of registers.  Each wave keeps the U rows of its 64 (NB=2) or 32
 // (NB=1) parents resident in registers for the whole kernel; the W tile is
 // staged through LDS by direct global->LDS loads (double-buffered,
-// XOR-swizzled 16-byte chunks) and
-// shared by all waves of the workgroup.  A workgroup covers one slice of the
+// XOR-swizzled 16-byte chunks) and shared by all waves of the workgroup;
+// so are the workgroup's L rows when parents are grouped by request.  A workgroup covers one slice of the
 // vocabulary for up to NB*NW*32 parents; slices x parent tiles form the grid.
 #pragma once
 #include "pct_device.h"
@@ -84,9 +84,9 @@ __device__ __forceinline__ void flush_lane(const K1Args& a, int p, int slice,
 }
 
 // Combine the (max, sum) partials of lanes l and l^32 (same parent).
-__device__ __forceinline__ void combine_halves(float& c2, float& s) {
-  float oc2 = __shfl_xor(c2, 32, kWave);
-  float os = __shfl_xor(s, 32, kWave);
+__device__ __forceinline__ void combine_halves(float& c2, float& s, int lane) {
+  float oc2 = swap_halves(c2, lane);
+  float os = swap_halves(s, lane);
   float m2 = fmaxf(c2, oc2);
   float r = 0.f;
   if (m2 != neg_inf()) {
@@ -97,38 +97,57 @@ __device__ __forceinline__ void combine_halves(float& c2, float& s) {
   s = r;
 }
 
-template <int NB, int NW, int R16>
+template <int NB, int NW, int R16, bool STAGED>
 __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
-  constexpr int NT = NW * 64;
   constexpr int CH = 2 * R16;               // 16-byte chunks per W row
   constexpr int TILE_CH = 64 * CH;          // chunks per 64-row tile
+  constexpr int SPAN = NW * NB * 32;        // parents per workgroup
+  constexpr int LS = STAGED ? kLdsRowSlots : 4;
+  // Double buffers as distinct LDS objects: the loop is unrolled by two so
+  // that every read names one buffer and every direct global->LDS load the
+  // other, which lets the compiler keep the next tile's loads in flight
+  // while the current tile is read (no conservative wait on aliasing).
+  __shared__ __align__(16) uint4 w0[TILE_CH];
+  __shared__ __align__(16) uint4 w1[TILE_CH];
+  __shared__ __align__(16) float4 l0[LS * 16];
+  __shared__ __align__(16) float4 l1[LS * 16];
   extern __shared__ __align__(16) unsigned char smem[];
-  uint4* wlds = reinterpret_cast<uint4*>(smem);  // [2][TILE_CH]
-  ZV* lists = reinterpret_cast<ZV*>(smem + 2 * TILE_CH * 16);
+  ZV* lists = reinterpret_cast<ZV*>(smem);
+  // per (lane, parent) list lengths live in LDS: only the rare path uses them
+  int* lcount = reinterpret_cast<int*>(lists + NW * 64 * NB * a.k);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, col = lane & 31;
   const int slice = blockIdx.x;
   const int t0 = slice * a.tiles_per_slice;
   const int t1 = min(t0 + a.tiles_per_slice, a.n_tiles);
-  const int pw = blockIdx.y * (NW * NB * 32) + wave * (NB * 32);
+  const int p0 = blockIdx.y * SPAN;
+  const int pw = p0 + wave * (NB * 32);
   const bool has_L = a.L != nullptr;
   const uint4* Wg = reinterpret_cast<const uint4*>(a.W);
+  // grouped rows of this workgroup: groups g0 .. g0 + nslots - 1
+  const int g0 = STAGED ? p0 / a.group_fp : 0;
+  const int nslots =
+      STAGED ? (min(p0 + SPAN, a.P) - 1) / a.group_fp - g0 + 1 : 0;
 
   bf16x8 uf[NB][R16];
   const float* lrow[NB];
+  int lslot[NB];
   float thr[NB], cm2[NB], ss[NB];
-  int cnt[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const int p = pw + 32 * b + col;
     const bool valid = p < a.P;
     const int pc = valid ? p : a.P - 1;
     const int tok = min(max(a.ptok[pc], 0), a.V - 1);
-    int64_t row =
-        a.plrow ? a.plrow[pc] : (int64_t)pc * a.lrow_mul + a.lrow_add;
+    lcount[(wave * 64 + lane) * NB + b] = 0;
+    int64_t row = a.plrow ? a.plrow[pc]
+                          : (int64_t)(a.group_fp > 0 ? pc / a.group_fp : pc) *
+                                    a.lrow_mul +
+                                a.lrow_add;
     row = row < 0 ? 0 : (row >= a.L_rows ? a.L_rows - 1 : row);
-    lrow[b] = has_L ? a.L + row * a.lstride : nullptr;
+    lrow[b] = (!STAGED && has_L) ? a.L + row * a.lstride : nullptr;
+    lslot[b] = STAGED ? pc / a.group_fp - g0 : 0;
     const uint4* up =
         reinterpret_cast<const uint4*>(a.U) + (int64_t)tok * CH + h;
 #pragma unroll
@@ -140,34 +159,56 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
     thr[b] = valid ? (a.theta ? a.theta[p] : neg_inf()) : pos_inf();
     cm2[b] = neg_inf();
     ss[b] = 0.f;
-    cnt[b] = 0;
   }
 
-  // W tile t -> LDS buffer buf by direct global->LDS loads: each wave
-  // instruction fills 64 consecutive 16-byte slots; slot q holds row q/CH,
-  // logical chunk (q%CH) ^ (row & (CH-1)).  Rows past V are clamped to row
-  // V-1 (their outputs are masked in the epilogue).
-  auto issue_tile = [&](int t, int buf) {
+  // Tile t -> LDS by direct global->LDS loads.  W: each wave instruction
+  // fills 64 consecutive 16-byte slots; slot q holds row q/CH, logical chunk
+  // (q%CH) ^ (row & (CH-1)), i.e. global chunk q ^ ((q/CH) & (CH-1)).  Rows
+  // past V are clamped to row V-1 (their outputs are masked).  L (staged):
+  // 16 chunks per row slot; V % 4 == 0 here, so a chunk is inside the row or
+  // wholly past V (then an in-bounds dummy that is never read).
+  constexpr int LMAX = (LS * 16 + 64 * NW - 1) / (64 * NW);  // L DMAs/wave
+  auto issue = [&](int t, uint4* wd, float4* ld) {
+    // L sources first: any register reload happens before DMAs are in
+    // flight, so it cannot make the wave wait for them
+    const float* lsrc[LMAX];
+    if (STAGED) {
+#pragma unroll
+      for (int i = 0; i < LMAX; ++i) {
+        const int c = (wave + i * NW) * 64 + lane;
+        const int slot = min(c >> 4, nslots - 1);
+        int64_t row = (int64_t)(g0 + slot) * a.lrow_mul + a.lrow_add;
+        row = row >= a.L_rows ? a.L_rows - 1 : row;
+        int v = 64 * t + 4 * (c & 15);
+        if (v >= a.V) v = 0;
+        lsrc[i] = a.L + row * a.lstride + v;
+      }
+    }
+    const uint4* wbase = Wg + (int64_t)64 * t * CH;
+    const bool wfull = 64 * t + 64 <= a.V;
 #pragma unroll
     for (int gi = wave; gi < TILE_CH / 64; gi += NW) {
       const int q = gi * 64 + lane;
       const int row = q / CH;
-      const int c = (q % CH) ^ (row & (CH - 1));
-      const int v = min(64 * t + row, a.V - 1);
-      __builtin_amdgcn_global_load_lds(
-          (gbl_ptr_t)(Wg + (int64_t)v * CH + c),
-          (lds_ptr_t)(wlds + buf * TILE_CH + gi * 64), 16, 0, 0);
+      int off = q ^ (row & (CH - 1));
+      if (!wfull && 64 * t + row >= a.V)
+        off = (a.V - 1 - 64 * t) * CH + (off % CH);
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(wbase + off),
+                                       (lds_ptr_t)(wd + gi * 64), 16, 0, 0);
+    }
+    if (STAGED) {
+#pragma unroll
+      for (int i = 0; i < LMAX; ++i) {
+        const int gi = wave + i * NW;
+        if (gi * 64 < nslots * 16)
+          __builtin_amdgcn_global_load_lds((gbl_ptr_t)lsrc[i],
+                                           (lds_ptr_t)(ld + gi * 64), 16, 0,
+                                           0);
+      }
     }
   };
 
-  if (t0 < t1) issue_tile(t0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  for (int t = t0; t < t1; ++t) {
-    const int buf = (t - t0) & 1;
-    if (t + 1 < t1) issue_tile(t + 1, buf ^ 1);
-    const uint4* wt = wlds + buf * TILE_CH;
+  auto compute = [&](int t, const uint4* wt, const float4* lt) {
     const bool full = 64 * t + 64 <= a.V;
 #pragma unroll
     for (int av = 0; av < 2; ++av) {
@@ -190,7 +231,29 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         float z[16];
-        if (full && a.vec_ok) {
+        if (STAGED) {
+          const float4* lp = lt + lslot[b] * 16 + 8 * av + h;
+          if (full) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const float4 l4 = lp[2 * g];
+              z[4 * g + 0] = l4.x + acc[b][4 * g + 0];
+              z[4 * g + 1] = l4.y + acc[b][4 * g + 1];
+              z[4 * g + 2] = l4.z + acc[b][4 * g + 2];
+              z[4 * g + 3] = l4.w + acc[b][4 * g + 3];
+            }
+          } else {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const float4 l4 = lp[2 * g];
+              const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                z[4 * g + e] = vb + 8 * g + e < a.V ? lv[e] + acc[b][4 * g + e]
+                                                     : neg_inf();
+            }
+          }
+        } else if (full && a.vec_ok) {
           if (has_L) {
             const float4* lp = reinterpret_cast<const float4*>(lrow[b] + vb);
 #pragma unroll
@@ -218,7 +281,7 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
         for (int j = 1; j < 16; ++j) m = fmaxf(m, z[j]);
 
         const int p = pw + 32 * b + col;
-        if (a.z_out != nullptr && p < a.P) {
+        if (!STAGED && a.z_out != nullptr && p < a.P) {
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
             const int v = vb + 8 * (j >> 2) + (j & 3);
@@ -248,7 +311,9 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
         const bool hit = m >= thr[b];
         if (__any(hit)) {
           if (hit) {
-            ZV* lst = lists + ((wave * 64 + lane) * NB + b) * a.k;
+            const int li = (wave * 64 + lane) * NB + b;
+            ZV* lst = lists + li * a.k;
+            int cnt = lcount[li];
             int v = vb;
 #pragma unroll 1
             for (int j = 0; j < 16; ++j) {
@@ -256,49 +321,64 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
 #pragma unroll
               for (int i = 0; i < 15; ++i) z[i] = z[i + 1];
               if (zj >= thr[b] && v < a.V)
-                list_insert(lst, a.k, cnt[b], thr[b], zj, v);
+                list_insert(lst, a.k, cnt, thr[b], zj, v);
               v += ((j & 3) == 3) ? 5 : 1;
             }
+            lcount[li] = cnt;
           }
         }
       }
     }
+  };
+
+  if (t0 < t1) issue(t0, w0, l0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int t = t0; t < t1; t += 2) {
+    if (t + 1 < t1) issue(t + 1, w1, l1);
+    compute(t, w0, l0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if (t + 1 < t1) {
+      if (t + 2 < t1) issue(t + 2, w0, l0);
+      compute(t + 1, w1, l1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
   }
 
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     float c2 = cm2[b], s = ss[b];
-    combine_halves(c2, s);
+    combine_halves(c2, s, lane);
     const int p = pw + 32 * b + col;
     if (p < a.P) {
-      ZV* lst = lists + ((wave * 64 + lane) * NB + b) * a.k;
-      flush_lane(a, p, slice, c2, s, lst, cnt[b], h == 0);
+      const int li = (wave * 64 + lane) * NB + b;
+      flush_lane(a, p, slice, c2, s, lists + li * a.k, lcount[li], h == 0);
     }
   }
 }
 
-
-template <int NB, int NW, int R16>
+template <int NB, int NW, int R16, bool STAGED>
 hipError_t go_mfma(const K1Plan& pl, const K1Args& a, hipStream_t s) {
-  auto fn = markov_topk_mfma<NB, NW, R16>;
+  auto fn = markov_topk_mfma<NB, NW, R16, STAGED>;
   hipError_t e = allow_lds(reinterpret_cast<const void*>(fn), pl.lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(fn, pl.grid, pl.block, pl.lds, s, a);
   return hipGetLastError();
 }
 
-// Launcher for one rank (r = 16*R16): picks the (NB, NW) instantiation.
-template <int R16>
+// Launcher for one rank (r = 16*R16) and row mode: picks the (NB, NW)
+// instantiation.
+template <int R16, bool STAGED>
 hipError_t launch_mfma_rank(const K1Plan& pl, const K1Args& a,
                             hipStream_t s) {
-  if (pl.NB == 1) return go_mfma<1, 1, R16>(pl, a, s);
+  if (pl.NB == 1) return go_mfma<1, 1, R16, STAGED>(pl, a, s);
   switch (pl.NW) {
-    case 8: return go_mfma<2, 8, R16>(pl, a, s);
-    case 4: return go_mfma<2, 4, R16>(pl, a, s);
-    case 2: return go_mfma<2, 2, R16>(pl, a, s);
-    default: return go_mfma<2, 1, R16>(pl, a, s);
+    case 8: return go_mfma<2, 8, R16, STAGED>(pl, a, s);
+    case 4: return go_mfma<2, 4, R16, STAGED>(pl, a, s);
+    case 2: return go_mfma<2, 2, R16, STAGED>(pl, a, s);
+    default: return go_mfma<2, 1, R16, STAGED>(pl, a, s);
   }
 }
 

@@ -1,0 +1,10 @@
+// k_markov_r16s.hip -- fused Markov kernel instantiations for rank 256,
+// L rows staged through LDS.
+#include "k_markov_impl.h"
+
+namespace pct {
+hipError_t launch_mfma_r16s(const K1Plan& pl, const K1Args& a,
+                          hipStream_t s) {
+  return launch_mfma_rank<16, true>(pl, a, s);
+}
+}  // namespace pct

@@ -35,13 +35,23 @@ __global__ __launch_bounds__(256) void row_top_kernel(const float* L, int V,
   if (vec_ok) {
     const float4* L4 = reinterpret_cast<const float4*>(Lr);
     const int n4 = V / 4;
-    for (int i = tid; i < n4; i += 256) {
-      const float4 x = L4[i];
-      const int v = 4 * i;
-      if (zv_before(x.x, v, bz, bv)) { bz = x.x; bv = v; }
-      if (zv_before(x.y, v + 1, bz, bv)) { bz = x.y; bv = v + 1; }
-      if (zv_before(x.z, v + 2, bz, bv)) { bz = x.z; bv = v + 2; }
-      if (zv_before(x.w, v + 3, bz, bv)) { bz = x.w; bv = v + 3; }
+    // four independent 16-byte loads in flight per thread
+    for (int i0 = tid; i0 < n4; i0 += 4 * 256) {
+      float4 x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * 256;
+        x[u] = i < n4 ? L4[i] : make_float4(neg_inf(), neg_inf(), neg_inf(),
+                                            neg_inf());
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int v = 4 * (i0 + u * 256);
+        if (zv_before(x[u].x, v, bz, bv)) { bz = x[u].x; bv = v; }
+        if (zv_before(x[u].y, v + 1, bz, bv)) { bz = x[u].y; bv = v + 1; }
+        if (zv_before(x[u].z, v + 2, bz, bv)) { bz = x[u].z; bv = v + 2; }
+        if (zv_before(x[u].w, v + 3, bz, bv)) { bz = x[u].w; bv = v + 3; }
+      }
     }
     for (int v = 4 * n4 + tid; v < V; v += 256)
       if (zv_before(Lr[v], v, bz, bv)) { bz = Lr[v]; bv = v; }
@@ -146,23 +156,36 @@ __device__ float seed_theta(const SeedArgs& sa, int ptok, int row, int lane) {
 // Merging the fused kernel's partials (one wave per parent).
 
 // log-normaliser from [S][P] partials (c in log2 units, s = sum 2^(.-c)),
-// combined in double.
+// in one pass over memory: each lane keeps a running (max, sum) with fp32
+// scale factors and a double sum; lanes combine by shuffles.
 __device__ float wave_merge_lse(const float* part_c, const float* part_s,
                                 int S, int P, int p, int lane) {
-  double cm = -__builtin_inf();
-  for (int s = lane; s < S; s += kWave) {
-    const double c = part_c[(int64_t)s * P + p];
-    cm = c > cm ? c : cm;
-  }
-  cm = wave_max(cm);
+  float cm = neg_inf();
   double acc = 0.0;
-  for (int s = lane; s < S; s += kWave) {
-    const float c = part_c[(int64_t)s * P + p];
-    const float v = part_s[(int64_t)s * P + p];
-    if (c != neg_inf() && v > 0.f) acc += (double)v * exp2((double)c - cm);
+  for (int s0 = 0; s0 < S; s0 += 4 * kWave) {
+    float c[4], v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = s0 + i * kWave + lane;
+      c[i] = s < S ? part_c[(int64_t)s * P + p] : neg_inf();
+      v[i] = s < S ? part_s[(int64_t)s * P + p] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (c[i] == neg_inf() || !(v[i] > 0.f)) continue;
+      if (c[i] > cm) {
+        acc = acc * (double)__builtin_amdgcn_exp2f(cm - c[i]) + (double)v[i];
+        cm = c[i];
+      } else {
+        acc += (double)v[i] * (double)__builtin_amdgcn_exp2f(c[i] - cm);
+      }
+    }
   }
+  const float gm = wave_max(cm);
+  acc = (cm == neg_inf()) ? 0.0
+                          : acc * (double)__builtin_amdgcn_exp2f(cm - gm);
   acc = wave_sum(acc);
-  return (float)(kLn2 * (cm + log2(acc)));
+  return (float)(kLn2 * ((double)gm + log2(acc)));
 }
 
 // The i-th best candidate (z desc, token asc) of a parent, i = 0..k-1, by k
@@ -173,6 +196,25 @@ __device__ void wave_topk(const float* gz, const int32_t* gv, int cnt, int k,
                           int lane, F&& emit) {
   float pz = pos_inf();
   int32_t pv = -1;
+  if (cnt <= kWave) {
+    // one candidate per lane, loaded once
+    const float cz = lane < cnt ? gz[lane] : neg_inf();
+    const int32_t cv = lane < cnt ? gv[lane] : 0x7fffffff;
+    for (int i = 0; i < k; ++i) {
+      float bz = neg_inf();
+      int32_t bv = 0x7fffffff;
+      if (zv_before(pz, pv, cz, cv)) {
+        bz = cz;
+        bv = cv;
+      }
+      wave_best_zv(bz, bv);
+      if (bv == 0x7fffffff) bv = 0;  // fewer than k candidates: cannot
+      emit(i, bz, bv);                // happen with a valid seed
+      pz = bz;
+      pv = bv;
+    }
+    return;
+  }
   for (int i = 0; i < k; ++i) {
     float bz = neg_inf();
     int32_t bv = 0x7fffffff;
@@ -185,11 +227,122 @@ __device__ void wave_topk(const float* gz, const int32_t* gv, int cnt, int k,
       }
     }
     wave_best_zv(bz, bv);
-    if (bv == 0x7fffffff) bv = 0;  // fewer than k candidates: cannot happen
-    emit(i, bz, bv);                // with a valid threshold seed
+    if (bv == 0x7fffffff) bv = 0;
+    emit(i, bz, bv);
     pz = bz;
     pv = bv;
   }
+}
+
+// Seeds of up to 32 parents that share one L row (one wave), computed with
+// the same bf16 MFMA as the fused kernel: the seed tokens form the 32 "vocab"
+// rows of a 32x32x16 block and the parents its columns.  A second MFMA on
+// |U|, |W| gives sum|u w| for the rounding margin.  Operands come from LDS
+// (staged by the caller): wrows[32][cs] and urows[32][cs] 16-byte chunks
+// (cs = r/8 + 1, one chunk of padding), lval[32] the seed tokens' logits,
+// vt[32] the seed tokens (-1 = none).  Returns the threshold of the parent
+// in column lane%32 (meaningful for columns < npar).
+__device__ float seed_theta_mfma(const SeedArgs& sa, const uint4* wrows,
+                                 const uint4* urows, const float* lval,
+                                 const int* vt, int lane) {
+  const int h = lane >> 5, col = lane & 31;
+  const int cs = sa.r / 8 + 1;
+  f32x16 acc, aacc;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    acc[j] = 0.f;
+    aacc[j] = 0.f;
+  }
+  for (int kk = 0; kk < sa.r / 16; ++kk) {
+    const uint4 w4 = wrows[col * cs + 2 * kk + h];
+    const uint4 u4 = urows[col * cs + 2 * kk + h];
+    const uint4 wa = make_uint4(w4.x & 0x7fff7fffu, w4.y & 0x7fff7fffu,
+                                w4.z & 0x7fff7fffu, w4.w & 0x7fff7fffu);
+    const uint4 ua = make_uint4(u4.x & 0x7fff7fffu, u4.y & 0x7fff7fffu,
+                                u4.z & 0x7fff7fffu, u4.w & 0x7fff7fffu);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        __builtin_bit_cast(bf16x8, w4), __builtin_bit_cast(bf16x8, u4), acc,
+        0, 0, 0);
+    aacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        __builtin_bit_cast(bf16x8, wa), __builtin_bit_cast(bf16x8, ua), aacc,
+        0, 0, 0);
+  }
+  // register j holds seed token 8*(j/4) + 4h + j%4 of this column's parent
+  float z[16];
+  float A = 0.f, zmax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int ti = 8 * (j >> 2) + 4 * h + (j & 3);
+    if (vt[ti] >= 0) {
+      z[j] = lval[ti] + acc[j];
+      A = fmaxf(A, aacc[j]);
+      zmax = fmaxf(zmax, fabsf(z[j]));
+    } else {
+      z[j] = neg_inf();
+    }
+  }
+  // k-th largest of the column's 32 values (16 here, 16 in lane^32)
+  uint32_t removed = 0;
+  float kth = neg_inf();
+  for (int r = 0; r < sa.k; ++r) {
+    float bz = neg_inf();
+    int bj = -1;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (!((removed >> j) & 1u) && z[j] > bz) {
+        bz = z[j];
+        bj = j;
+      }
+    const float oz = swap_halves(bz, lane);
+    const bool mine = bz > oz || (bz == oz && h == 0);
+    if (mine && bj >= 0) removed |= 1u << bj;
+    kth = fmaxf(bz, oz);
+  }
+  A = fmaxf(A, swap_halves(A, lane));
+  zmax = fmaxf(zmax, swap_halves(zmax, lane));
+  const float margin = 4.f * (float)sa.r * 5.9604645e-8f * A +
+                       4.f * 1.1920929e-7f * zmax + 1e-30f;
+  return kth - margin;
+}
+
+// Cooperative staging of the seed operands of L row `row`: the kSeedT seed
+// tokens, their logits and W rows (all threads of the block take part).
+__device__ void stage_seed_rows(const SeedArgs& sa, int row, uint4* wrows,
+                                float* lval, int* vt, int tid, int nthr) {
+  const int* rt = sa.rowtop + (int64_t)row * kSeedT;
+  const int ch = sa.r / 8, cs = ch + 1;
+  for (int i = tid; i < kSeedT * ch; i += nthr) {
+    const int t = i / ch, c = i % ch;
+    const int v = rt[t];
+    const int vv = (v >= 0 && v < sa.V) ? v : 0;
+    wrows[t * cs + c] =
+        reinterpret_cast<const uint4*>(sa.W)[(int64_t)vv * ch + c];
+  }
+  for (int t = tid; t < kSeedT; t += nthr) {
+    const int v = rt[t];
+    const bool ok = v >= 0 && v < sa.V;
+    vt[t] = ok ? v : -1;
+    lval[t] = ok ? sa.L[(int64_t)row * sa.lstride + v] : 0.f;
+  }
+}
+
+// Cooperative staging of the U rows of up to 32 parents.
+__device__ void stage_parent_rows(const SeedArgs& sa, const int32_t* ptok,
+                                  int npar, uint4* urows, int tid, int nthr) {
+  const int ch = sa.r / 8, cs = ch + 1;
+  for (int i = tid; i < 32 * ch; i += nthr) {
+    const int t = i / ch, c = i % ch;
+    const int tok = t < npar ? min(max(ptok[t], 0), sa.V - 1) : 0;
+    urows[t * cs + c] =
+        reinterpret_cast<const uint4*>(sa.U)[(int64_t)tok * ch + c];
+  }
+}
+
+constexpr int kSeedRowChunks = 256 / 8 + 1;  // r <= 256, one pad chunk
+
+__device__ __forceinline__ bool seed_by_mfma(const SeedArgs& sa) {
+  return sa.use_seed && sa.U != nullptr && sa.uw_bf16 && sa.r % 16 == 0 &&
+         sa.r <= 256 && sa.k <= kSeedT;
 }
 
 // ---------------------------------------------------------------------
@@ -197,9 +350,21 @@ __device__ void wave_topk(const float* gz, const int32_t* gv, int cnt, int k,
 __global__ __launch_bounds__(64) void init_kernel(int B, const int32_t* anchor,
                                                   Frontier f, int32_t* gcnt,
                                                   SeedArgs sa) {
+  __shared__ uint4 wrows[kSeedT * kSeedRowChunks];
+  __shared__ uint4 urows[32 * kSeedRowChunks];
+  __shared__ float lval[kSeedT];
+  __shared__ int vt[kSeedT];
   const int q = blockIdx.x, lane = threadIdx.x;
   const int a = anchor[q];
-  const float th = seed_theta(sa, a, q * B, lane);
+  float th;
+  if (seed_by_mfma(sa)) {
+    stage_seed_rows(sa, q * B, wrows, lval, vt, lane, 64);
+    stage_parent_rows(sa, anchor + q, 1, urows, lane, 64);
+    __syncthreads();
+    th = seed_theta_mfma(sa, wrows, urows, lval, vt, lane);
+  } else {
+    th = seed_theta(sa, a, q * B, lane);
+  }
   if (lane == 0) {
     f.tok[q] = a;
     f.pid[q] = -1;
@@ -212,21 +377,33 @@ __global__ __launch_bounds__(64) void init_kernel(int B, const int32_t* anchor,
 
 // One workgroup per request: children of every frontier parent, their
 // scores and pool keys, the beam of the next depth and its seeds.
-__global__ __launch_bounds__(256) void expand_kernel(ExpandArgs a) {
+constexpr int kExpandWaves = 16;
+__global__ __launch_bounds__(kExpandWaves * 64) void expand_kernel(
+    ExpandArgs a) {
   __shared__ uint64_t ckey[kMaxCand];
   __shared__ int32_t cpid[kMaxCand];
   __shared__ int32_t ntok[kMaxCand];
+  __shared__ uint4 wrows[kSeedT * kSeedRowChunks];
+  __shared__ uint4 urows[32 * kSeedRowChunks];
+  __shared__ float lval[kSeedT];
+  __shared__ int vt[kSeedT];
   const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63,
             wave = tid >> 6;
   const int NC = a.Fp * a.k;
-  for (int j = wave; j < a.Fp; j += 4) {
+  const int row = q * a.B + a.d;  // L row of depth d+1
+  const bool mseed = a.d < a.B && seed_by_mfma(a.seed);
+  // the next depth's seed tokens are known already: stage their W rows and
+  // logits now, overlapping the merge below
+  if (mseed)
+    stage_seed_rows(a.seed, row, wrows, lval, vt, tid, kExpandWaves * 64);
+  for (int j = wave; j < a.Fp; j += kExpandWaves) {
     const int p = q * a.Fp + j;
     const int sp = a.shared_stats ? q : p;
-    const float lse =
-        wave_merge_lse(a.part_c, a.part_s, a.n_slices, a.Pstat, sp, lane);
     const float sp_score = a.cur.s[p];
     const int ppid = a.cur.pid[p];
     const int cnt = min(a.gcnt[sp], a.cap);
+    const float lse =
+        wave_merge_lse(a.part_c, a.part_s, a.n_slices, a.Pstat, sp, lane);
     wave_topk(a.gz + (int64_t)sp * a.cap, a.gv + (int64_t)sp * a.cap, cnt,
               a.k, lane, [&](int i, float z, int32_t v) {
                 if (lane == 0) {
@@ -242,27 +419,42 @@ __global__ __launch_bounds__(256) void expand_kernel(ExpandArgs a) {
               });
   }
   __syncthreads();
-  // beam: the Fn smallest keys of this depth's children, by rank (keys are
+  // beam: the Fn smallest keys of this depth's children (keys are
   // distinct: (parent, token) pairs are unique)
-  for (int c = tid; c < NC; c += 256) {
+  auto emit_beam = [&](int rank, uint64_t key, int pid) {
+    const int o = q * a.Fn + rank;
+    a.nxt.tok[o] = key_tok(key);
+    a.nxt.pid[o] = pid;
+    a.nxt.s[o] = key_score(key);
+    a.nxt.lrow[o] = q * a.B + a.d;  // row of depth d+1
+    ntok[rank] = key_tok(key);
+    if (a.gcnt_next) a.gcnt_next[o] = 0;
+  };
+  for (int c = tid; c < NC; c += kExpandWaves * 64) {
     const uint64_t key = ckey[c];
     int rank = 0;
     for (int o = 0; o < NC; ++o) rank += ckey[o] < key;
-    if (rank < a.Fn) {
-      const int o = q * a.Fn + rank;
-      a.nxt.tok[o] = key_tok(key);
-      a.nxt.pid[o] = cpid[c];
-      a.nxt.s[o] = key_score(key);
-      a.nxt.lrow[o] = q * a.B + a.d;  // row of depth d+1
-      ntok[rank] = key_tok(key);
-      if (a.gcnt_next) a.gcnt_next[o] = 0;
-    }
+    if (rank < a.Fn) emit_beam(rank, key, cpid[c]);
   }
   if (a.d >= a.B) return;
   __syncthreads();
-  for (int i = wave; i < a.Fn; i += 4) {
-    const float th = seed_theta(a.seed, ntok[i], q * a.B + a.d, lane);
-    if (lane == 0) a.nxt.theta[q * a.Fn + i] = th;
+  if (mseed) {
+    for (int base = 0; base < a.Fn; base += 32) {
+      const int np = min(32, a.Fn - base);
+      stage_parent_rows(a.seed, ntok + base, np, urows, tid,
+                        kExpandWaves * 64);
+      __syncthreads();
+      if (wave == 0) {
+        const float th = seed_theta_mfma(a.seed, wrows, urows, lval, vt, lane);
+        if (lane < np) a.nxt.theta[q * a.Fn + base + lane] = th;
+      }
+      __syncthreads();
+    }
+  } else {
+    for (int i = wave; i < a.Fn; i += kExpandWaves) {
+      const float th = seed_theta(a.seed, ntok[i], row, lane);
+      if (lane == 0) a.nxt.theta[q * a.Fn + i] = th;
+    }
   }
 }
 
@@ -363,7 +555,8 @@ hipError_t launch_init(int batch, int B, const int32_t* anchor, Frontier f,
 }
 
 hipError_t launch_expand(const ExpandArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(expand_kernel, dim3(a.batch), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(expand_kernel, dim3(a.batch), dim3(kExpandWaves * 64), 0,
+                     s, a);
   return hipGetLastError();
 }
 

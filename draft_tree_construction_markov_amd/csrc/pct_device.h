@@ -59,42 +59,121 @@ __device__ __forceinline__ bool zv_before(float za, int32_t va, float zb,
 }
 
 // ---------------------------------------------------------------------
-// wave reductions (64 lanes)
+// Wave-wide all-reductions (64 lanes) on DPP: within each row of 16 lanes a
+// quad xor-1 / xor-2 exchange and row rotations by 4 and 8 give every lane
+// its row's result; the four row results are then read with readlane, so
+// the result is the same on every lane.  (Cross-lane shuffles through
+// ds_bpermute have a long latency; these are VALU modifiers.)
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_mov_dpp(x, CTRL, 0xf, 0xf, false);
+}
+constexpr int kDppXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kDppRor4 = 0x124; // row_ror:4
+constexpr int kDppRor8 = 0x128; // row_ror:8
+
 template <typename T>
-__device__ __forceinline__ T wave_max(T x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    T y = __shfl_xor(x, o, kWave);
-    x = y > x ? y : x;
+struct Bits32 {
+  static __device__ __forceinline__ int to(T x) {
+    return __builtin_bit_cast(int, x);
   }
-  return x;
-}
-template <typename T>
-__device__ __forceinline__ T wave_min(T x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    T y = __shfl_xor(x, o, kWave);
-    x = y < x ? y : x;
+  static __device__ __forceinline__ T from(int x) {
+    return __builtin_bit_cast(T, x);
   }
-  return x;
+};
+
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_allreduce32(T x, Op op) {
+  x = op(x, Bits32<T>::from(dpp_i<kDppXor1>(Bits32<T>::to(x))));
+  x = op(x, Bits32<T>::from(dpp_i<kDppXor2>(Bits32<T>::to(x))));
+  x = op(x, Bits32<T>::from(dpp_i<kDppRor4>(Bits32<T>::to(x))));
+  x = op(x, Bits32<T>::from(dpp_i<kDppRor8>(Bits32<T>::to(x))));
+  const int b = Bits32<T>::to(x);
+  const T r0 = Bits32<T>::from(__builtin_amdgcn_readlane(b, 0));
+  const T r1 = Bits32<T>::from(__builtin_amdgcn_readlane(b, 16));
+  const T r2 = Bits32<T>::from(__builtin_amdgcn_readlane(b, 32));
+  const T r3 = Bits32<T>::from(__builtin_amdgcn_readlane(b, 48));
+  return op(op(r0, r1), op(r2, r3));
 }
-template <typename T>
-__device__ __forceinline__ T wave_sum(T x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
-  return x;
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const int lo = dpp_i<CTRL>((int)(uint32_t)u);
+  const int hi = dpp_i<CTRL>((int)(uint32_t)(u >> 32));
+  return __builtin_bit_cast(double,
+                            ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
 }
+__device__ __forceinline__ double readlane_d(double x, int l) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+template <typename Op>
+__device__ __forceinline__ double wave_allreduce_d(double x, Op op) {
+  x = op(x, dpp_d<kDppXor1>(x));
+  x = op(x, dpp_d<kDppXor2>(x));
+  x = op(x, dpp_d<kDppRor4>(x));
+  x = op(x, dpp_d<kDppRor8>(x));
+  return op(op(readlane_d(x, 0), readlane_d(x, 16)),
+            op(readlane_d(x, 32), readlane_d(x, 48)));
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+  return wave_allreduce32(x, [](float a, float b) { return fmaxf(a, b); });
+}
+__device__ __forceinline__ int wave_max(int x) {
+  return wave_allreduce32(x, [](int a, int b) { return a > b ? a : b; });
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  return wave_allreduce32(x, [](float a, float b) { return a + b; });
+}
+__device__ __forceinline__ double wave_sum(double x) {
+  return wave_allreduce_d(x, [](double a, double b) { return a + b; });
+}
+__device__ __forceinline__ double wave_max(double x) {
+  return wave_allreduce_d(x, [](double a, double b) { return a > b ? a : b; });
+}
+
 // best (z desc, v asc) pair over the wave, result on every lane
 __device__ __forceinline__ void wave_best_zv(float& z, int32_t& v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    float z2 = __shfl_xor(z, o, kWave);
-    int32_t v2 = __shfl_xor(v, o, kWave);
+  auto step = [&](float z2, int32_t v2) {
     if (zv_before(z2, v2, z, v)) {
       z = z2;
       v = v2;
     }
+  };
+  step(Bits32<float>::from(dpp_i<kDppXor1>(Bits32<float>::to(z))),
+       dpp_i<kDppXor1>(v));
+  step(Bits32<float>::from(dpp_i<kDppXor2>(Bits32<float>::to(z))),
+       dpp_i<kDppXor2>(v));
+  step(Bits32<float>::from(dpp_i<kDppRor4>(Bits32<float>::to(z))),
+       dpp_i<kDppRor4>(v));
+  step(Bits32<float>::from(dpp_i<kDppRor8>(Bits32<float>::to(z))),
+       dpp_i<kDppRor8>(v));
+  const int zb = Bits32<float>::to(z);
+  float bz = Bits32<float>::from(__builtin_amdgcn_readlane(zb, 0));
+  int32_t bv = __builtin_amdgcn_readlane(v, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r) {
+    const float z2 = Bits32<float>::from(__builtin_amdgcn_readlane(zb, 16 * r));
+    const int32_t v2 = __builtin_amdgcn_readlane(v, 16 * r);
+    if (zv_before(z2, v2, bz, bv)) {
+      bz = z2;
+      bv = v2;
+    }
   }
+  z = bz;
+  v = bv;
+}
+
+// The value held by lane (lane ^ 32), via the gfx950 permlane32 swap.
+__device__ __forceinline__ float swap_halves(float x, int lane) {
+  const int b = Bits32<float>::to(x);
+  const auto pr = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  return Bits32<float>::from(lane < 32 ? pr[1] : pr[0]);
 }
 
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {

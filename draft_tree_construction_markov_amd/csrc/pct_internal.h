@@ -27,6 +27,11 @@ struct K1Args {
   const int32_t* plrow;  // [P] L row of each parent (null: p*lrow_mul+lrow_add)
   int lrow_mul, lrow_add;
   int64_t L_rows;        // rows of L (row indices are clamped to it)
+  // Grouped rows: when group_fp > 0 and plrow is null, parent p reads row
+  // (p / group_fp) * lrow_mul + lrow_add, and the fused kernel stages the
+  // workgroup's distinct rows of each vocabulary tile through LDS
+  // (lslots row slots per buffer).
+  int group_fp, lslots;
   const float* theta;    // [P] candidate threshold seeds (null: -inf)
   int tiles_per_slice, n_tiles, n_slices;  // mfma: 64-vocab tiles
   int vslice;                              // simple: vocab per slice
@@ -44,13 +49,16 @@ enum K1Kind { K1_MFMA = 0, K1_SIMPLE = 1 };
 struct K1Plan {
   int kind;
   int NB, NW, R16;
+  int lslots;  // LDS row slots for grouped rows (0: rows read directly)
   int n_tiles, tiles_per_slice, n_slices, vslice;
   int cap;  // candidate capacity per parent
-  size_t lds;
+  size_t lds;        // dynamic LDS bytes of the launch
+  size_t lds_total;  // static + dynamic, for occupancy planning
   dim3 grid, block;
 };
 
 constexpr int kSeedT = 32;         // top tokens of each L row used for seeds
+constexpr int kLdsRowSlots = 36;   // staged L rows per buffer (fused kernel)
 constexpr int kSimpleThreads = 128;
 constexpr int kMaxPool = 8192;     // generated children per request
 constexpr int kMaxCand = 2048;     // children per request and depth
@@ -93,7 +101,7 @@ class ProfScope {
 };
 
 K1Plan plan_k1(int P, int V, int r, int k, int uw_dtype, bool has_uw,
-               bool allow_mfma = true);
+               bool allow_mfma = true, int group_fp = 0);
 hipError_t launch_k1(const K1Plan& pl, const K1Args& a, hipStream_t s);
 
 // Per-request state of the depth loop.
