@@ -305,16 +305,18 @@ int ref_greedy_chain(int32_t B, int32_t V, int32_t r, const float* L,
 typedef struct {
   float s;
   int32_t pout; /* parent's output index, -1 = root */
+  int32_t rank; /* position in the parent's child list, (z desc, tok asc) */
   int32_t tok;
   int32_t depth;
 } hnode_t;
 
-/* K' = (s desc, parent output index asc, token asc); returns 1 if a goes
- * first */
+/* K' = (s desc, parent output index asc, child rank asc); the child rank
+ * orders siblings by (z desc, token asc), so equal logits fall back to the
+ * token.  Returns 1 if a goes first. */
 static int hfirst(const hnode_t* a, const hnode_t* b) {
   if (a->s != b->s) return a->s > b->s;
   if (a->pout != b->pout) return a->pout < b->pout;
-  return a->tok < b->tok;
+  return a->rank < b->rank;
 }
 
 typedef struct {
@@ -392,6 +394,7 @@ static int push_children(heap_t* h, int32_t B, int32_t V, int32_t r,
     c.s = ps + l;
     c.s = c.s + 0.0f;
     c.pout = pout;
+    c.rank = i;
     c.tok = ct[i];
     c.depth = d;
     int rc = heap_push(h, c);

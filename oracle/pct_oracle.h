@@ -90,7 +90,8 @@ int ref_greedy_chain(int32_t B, int32_t V, int32_t r, const float* L,
                      int32_t anchor, int32_t* chain);
 
 /* Greedy best-first tree of one request: repeatedly take the prefix with the
- * highest probability, key K' = (s desc, parent output index asc, token asc).
+ * highest probability, key K' = (s desc, parent output index asc, child rank
+ * asc), where the child rank orders siblings by (z desc, token asc).
  * U/W NULL => marginal rows (block-diffusion drafter); otherwise children are
  * conditioned on the parent token.  Children are restricted to the
  * min(n_max, V) best tokens of their row (exact: a prefix among the n best has
