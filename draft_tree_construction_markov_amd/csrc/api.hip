@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "../../include/pctree.h"
 #include "pct_internal.h"
 
@@ -439,6 +441,131 @@ pct_status pct_build_tree(const pct_tree_shape* shape, const float* L,
       ProfScope ps(PROF_MASK, batch, s);
       e = launch_mask(batch, sh.N, parent, n_nodes, mask, s);
     }
+    if (e != hipSuccess) return hip_fail(e, "mask kernel");
+  }
+  return PCT_OK;
+}
+
+// ------------------------------------------------------------------------
+namespace {
+struct AdaptiveWs {
+  float* lse_f;
+  int32_t* ltok_f;
+  float* llp_f;
+  int32_t* flag;
+  float* lse_s;
+  int32_t* ltok_s;
+  float* llp_s;
+};
+size_t carve_adaptive(int batch, int B, int V, int n_max, void* ws,
+                      AdaptiveWs& w, int& Kf, int& Ks) {
+  const int64_t rows = (int64_t)batch * B;
+  Kf = std::min(std::min(kAdaptiveShortList, n_max), V);
+  Ks = std::min(n_max, V);
+  Carve c{static_cast<char*>(ws)};
+  w.lse_f = c.take<float>(rows);
+  w.ltok_f = c.take<int32_t>(rows * Kf);
+  w.llp_f = c.take<float>(rows * Kf);
+  w.flag = c.take<int32_t>(batch);
+  w.lse_s = c.take<float>(rows);
+  w.ltok_s = c.take<int32_t>(rows * Ks);
+  w.llp_s = c.take<float>(rows * Ks);
+  return c.off;
+}
+pct_status check_adaptive(int32_t batch, int32_t B, int32_t V, int32_t n_max) {
+  if (batch < 1 || B < 1 || V < 1 || n_max < 1)
+    return fail(PCT_ERR_INVALID_ARG, "need batch, B, V, n_max >= 1");
+  if (V >= (1 << 18)) return fail(PCT_ERR_INVALID_ARG, "V must be < 2^18");
+  if (B > 255)
+    return fail(PCT_ERR_UNSUPPORTED, "B = %d exceeds 255", B);
+  if (n_max > kAdaptiveMaxNodes)
+    return fail(PCT_ERR_UNSUPPORTED, "n_max = %d exceeds %d", n_max,
+                kAdaptiveMaxNodes);
+  return PCT_OK;
+}
+}  // namespace
+
+size_t pct_build_tree_adaptive_workspace(int32_t batch, int32_t B, int32_t V,
+                                         int32_t n_max) {
+  if (check_adaptive(batch, B, V, n_max) != PCT_OK) return 0;
+  AdaptiveWs w;
+  int Kf, Ks;
+  return carve_adaptive(batch, B, V, n_max, nullptr, w, Kf, Ks);
+}
+
+pct_status pct_build_tree_adaptive(int32_t batch, int32_t B, int32_t V,
+                                   int32_t n_max, const float* L,
+                                   const int32_t* ctx_len,
+                                   const pct_cost_model* cost, int32_t* tok,
+                                   int32_t* parent, int32_t* depth,
+                                   float* score, int32_t* n_star, double* phi,
+                                   double* throughput, uint64_t* mask,
+                                   void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  pct_status st = check_adaptive(batch, B, V, n_max);
+  if (st != PCT_OK) return st;
+  if (!L || !tok || !parent || !depth || !score || !n_star || !phi ||
+      !throughput || !workspace || (cost && !ctx_len))
+    return fail(PCT_ERR_INVALID_ARG, "required pointer is NULL");
+  if (cost) {
+    if (!(cost->c1 >= 0.0) || !(cost->c2 >= 0.0) || !(cost->c_ell >= 0.0))
+      return fail(PCT_ERR_INVALID_ARG,
+                  "cost model must be convex and increasing (c1, c2, c_ell "
+                  ">= 0)");
+    if (!(cost->C_d + cost->c0 > 0.0))
+      return fail(PCT_ERR_INVALID_ARG, "round cost at n = 0 must be > 0");
+  }
+  AdaptiveWs w;
+  int Kf, Ks;
+  const size_t need = carve_adaptive(batch, B, V, n_max, nullptr, w, Kf, Ks);
+  if (workspace_bytes < need)
+    return fail(PCT_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  carve_adaptive(batch, B, V, n_max, workspace, w, Kf, Ks);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int rows = batch * B;
+  const int vec_ok = aligned16(L) && V % 4 == 0;
+  double c5[5] = {0, 0, 0, 0, 0};
+  if (cost) {
+    c5[0] = cost->C_d;
+    c5[1] = cost->c0;
+    c5[2] = cost->c1;
+    c5[3] = cost->c2;
+    c5[4] = cost->c_ell;
+  }
+  const double* cp = cost ? c5 : nullptr;
+  hipError_t e;
+  {
+    ProfScope ps(PROF_ROWSTATS, rows, s);
+    e = launch_rowsel(L, rows, V, B, Kf, Kf, nullptr, vec_ok, w.lse_f,
+                      w.ltok_f, w.llp_f, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "row statistics kernel");
+  {
+    ProfScope ps(PROF_BESTFIRST, batch, s);
+    e = launch_bestfirst(batch, B, V, n_max, Kf, Kf, Kf < V, w.ltok_f, w.llp_f,
+                         ctx_len, cp, tok, parent, depth, score, n_star, phi,
+                         throughput, w.flag, 0, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "best-first kernel");
+  if (Ks > Kf) {
+    // requests whose tree outgrew the short lists: full-length lists
+    {
+      ProfScope ps(PROF_ROWSTATS, 0, s);
+      e = launch_rowsel(L, rows, V, B, Ks, Ks, w.flag, vec_ok, w.lse_s,
+                        w.ltok_s, w.llp_s, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "row statistics kernel");
+    {
+      ProfScope ps(PROF_BESTFIRST, 0, s);
+      e = launch_bestfirst(batch, B, V, n_max, Ks, Ks, Ks < V, w.ltok_s,
+                           w.llp_s, ctx_len, cp, tok, parent, depth, score,
+                           n_star, phi, throughput, w.flag, 1, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "best-first kernel");
+  }
+  if (mask) {
+    ProfScope ps(PROF_MASK, batch, s);
+    e = launch_mask(batch, n_max, parent, n_star, mask, s);
     if (e != hipSuccess) return hip_fail(e, "mask kernel");
   }
   return PCT_OK;

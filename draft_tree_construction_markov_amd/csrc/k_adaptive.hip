@@ -1,0 +1,441 @@
+// k_adaptive.hip -- the adaptive best-first draft tree over a block-diffusion
+// drafter's per-position marginals (CaDDTree summary, "Method": for a fixed
+// node count the best tree takes prefixes in order of probability; nodes are
+// added one at a time and the build stops as soon as the throughput
+// (1 + Phi) / (C_d + C_v(n; l)) no longer increases).
+//
+// Two kernels:
+//  rowsel_kernel    one workgroup per logit row: streaming log-sum-exp and
+//                   the row's best K tokens (logit desc, token asc), exact:
+//                   a pass computes per-thread bests, the K-th best of those
+//                   bounds the row's K-th best from below, a second pass
+//                   collects every element not after that bound, ranks them.
+//  bestfirst_kernel one wave per request: lazy best-first expansion (a popped
+//                   node pushes its next sibling and its first child) over
+//                   the per-depth lists, with the stop test evaluated before
+//                   every pop.  Exact while every needed child rank is inside
+//                   the lists; a request that outgrows short lists is flagged
+//                   and rebuilt from full-length lists.
+#include "pct_device.h"
+#include "pct_internal.h"
+
+namespace pct {
+
+constexpr int kRowThreads = 1024;
+constexpr int kRowCap = 4096;       // LDS candidate buffer of rowsel
+constexpr int kFrontierCap = 4096;  // LDS frontier of bestfirst
+
+struct RowSelArgs {
+  const float* L;
+  int V, B, K, kstride;
+  const int32_t* only_flagged;  // null: every row; else rows of flagged reqs
+  int vec_ok;
+  float* lse;     // [rows]
+  int32_t* ltok;  // [rows][kstride]
+  float* llp;     // [rows][kstride]  log pi = fp32(L - lse)
+};
+
+__device__ __forceinline__ bool not_after(float z, int v, float tz, int tv) {
+  return zv_before(z, v, tz, tv) || (z == tz && v == tv);
+}
+
+__global__ __launch_bounds__(kRowThreads) void rowsel_kernel(RowSelArgs a) {
+  __shared__ float tbz[kRowThreads];
+  __shared__ int tbv[kRowThreads];
+  __shared__ float cz[kRowCap];
+  __shared__ int cv[kRowCap];
+  __shared__ float wm[kRowThreads / kWave];
+  __shared__ double ws[kRowThreads / kWave];
+  __shared__ int s_count;
+  __shared__ float s_tz;
+  __shared__ int s_tv;
+  __shared__ float s_lse;
+  const int row = blockIdx.x;
+  if (a.only_flagged && !a.only_flagged[row / a.B]) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* Lr = a.L + (int64_t)row * a.V;
+
+  // pass 1: online log-sum-exp (log2 units) and the thread's best element
+  float m2 = neg_inf(), S = 0.f, bz = neg_inf();
+  int bv = 0x7fffffff;
+  auto visit = [&](float z, int v) {
+    const float z2 = z * kLog2e;
+    if (z2 > m2) {
+      S = S * __builtin_amdgcn_exp2f(m2 - z2) + 1.f;
+      m2 = z2;
+    } else {
+      S += __builtin_amdgcn_exp2f(z2 - m2);
+    }
+    if (zv_before(z, v, bz, bv)) {
+      bz = z;
+      bv = v;
+    }
+  };
+  const int n4 = a.vec_ok ? a.V / 4 : 0;
+  const float4* L4 = reinterpret_cast<const float4*>(Lr);
+  for (int i0 = tid; i0 < n4; i0 += 4 * kRowThreads) {
+    float4 x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * kRowThreads;
+      x[u] = i < n4 ? L4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * kRowThreads;
+      if (i < n4) {
+        visit(x[u].x, 4 * i);
+        visit(x[u].y, 4 * i + 1);
+        visit(x[u].z, 4 * i + 2);
+        visit(x[u].w, 4 * i + 3);
+      }
+    }
+  }
+  for (int v = 4 * n4 + tid; v < a.V; v += kRowThreads) visit(Lr[v], v);
+
+  // block log-sum-exp: lanes -> waves -> block, combined in double
+  {
+    const float wmax = wave_max(m2);
+    const float sc = (m2 == neg_inf()) ? 0.f
+                                       : S * __builtin_amdgcn_exp2f(m2 - wmax);
+    const double wsum = wave_sum((double)sc);
+    if (lane == 0) {
+      wm[wave] = wmax;
+      ws[wave] = wsum;
+    }
+  }
+  tbz[tid] = bz;
+  tbv[tid] = bv;
+  if (tid == 0) {
+    s_count = 0;
+    s_tz = neg_inf();  // "take everything" unless a K-th best exists
+    s_tv = 0x7fffffff;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float M = wm[0];
+    for (int w = 1; w < kRowThreads / kWave; ++w) M = fmaxf(M, wm[w]);
+    double tot = 0.0;
+    for (int w = 0; w < kRowThreads / kWave; ++w)
+      if (wm[w] != neg_inf()) tot += ws[w] * exp2((double)wm[w] - M);
+    s_lse = (float)(kLn2 * ((double)M + log2(tot)));
+  }
+
+  // bound: the K-th best of the group bests (K <= 256: groups of 4 threads)
+  // or of the thread bests; K distinct elements are not after it, so it
+  // cannot be after the row's K-th best
+  if (a.K <= 256) {
+    float gz = neg_inf();
+    int gv = 0x7fffffff;
+    if (tid < 256) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (zv_before(tbz[4 * tid + i], tbv[4 * tid + i], gz, gv)) {
+          gz = tbz[4 * tid + i];
+          gv = tbv[4 * tid + i];
+        }
+    }
+    __syncthreads();
+    if (tid < 256) {
+      tbz[tid] = gz;
+      tbv[tid] = gv;
+    }
+    __syncthreads();
+    if (tid < 256) {
+      int rank = 0;
+      for (int j = 0; j < 256; ++j) rank += zv_before(tbz[j], tbv[j], gz, gv);
+      if (rank == a.K - 1) {
+        s_tz = gz;
+        s_tv = gv;
+      }
+    }
+  } else {
+    int rank = 0;
+    for (int j = 0; j < kRowThreads; ++j)
+      rank += zv_before(tbz[j], tbv[j], bz, bv);
+    if (rank == a.K - 1) {
+      s_tz = bz;
+      s_tv = bv;
+    }
+  }
+  __syncthreads();
+  float tz = s_tz;
+  int tv = s_tv;
+  if (tv == 0x7fffffff) tz = neg_inf();  // fewer than K elements: take all
+
+  // pass 2 (repeated while the buffer overflows): collect every element not
+  // after the bound
+  for (;;) {
+    if (tid == 0) s_count = 0;
+    __syncthreads();
+    auto offer = [&](float z, int v, bool valid) {
+      const bool take = valid && not_after(z, v, tz, tv);
+      const uint64_t bal = __ballot(take);
+      if (bal == 0) return;
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&s_count, __popcll(bal));
+      base = __builtin_amdgcn_readfirstlane(base);
+      if (take) {
+        const int pos =
+            base + __builtin_amdgcn_mbcnt_hi(
+                       (uint32_t)(bal >> 32),
+                       __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+        if (pos < kRowCap) {
+          cz[pos] = z;
+          cv[pos] = v;
+        }
+      }
+    };
+    for (int i0 = wave * kWave; i0 < n4; i0 += kRowThreads) {
+      const int i = i0 + lane;
+      const bool ok = i < n4;
+      const float4 x = ok ? L4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      offer(x.x, 4 * i, ok);
+      offer(x.y, 4 * i + 1, ok);
+      offer(x.z, 4 * i + 2, ok);
+      offer(x.w, 4 * i + 3, ok);
+    }
+    for (int v0 = 4 * n4 + wave * kWave; v0 < a.V; v0 += kRowThreads) {
+      const int v = v0 + lane;
+      offer(v < a.V ? Lr[v] : 0.f, v, v < a.V);
+    }
+    __syncthreads();
+    const int count = s_count;
+    if (count <= kRowCap) break;
+    // overflow: the K-th best of the kRowCap collected elements is a
+    // tighter bound; at least kRowCap - K elements drop out per round
+    for (int e = tid; e < kRowCap; e += kRowThreads) {
+      int rank = 0;
+      for (int j = 0; j < kRowCap; ++j) rank += zv_before(cz[j], cv[j], cz[e], cv[e]);
+      if (rank == a.K - 1) {
+        s_tz = cz[e];
+        s_tv = cv[e];
+      }
+    }
+    __syncthreads();
+    tz = s_tz;
+    tv = s_tv;
+  }
+  const int count = s_count;
+  const float lse = s_lse;
+  // rank the collected elements; the first K form the list
+  const int klist = min(a.K, count);
+  for (int e = tid; e < count; e += kRowThreads) {
+    const float z = cz[e];
+    const int v = cv[e];
+    int rank = 0;
+    for (int j = 0; j < count; ++j) rank += zv_before(cz[j], cv[j], z, v);
+    if (rank < klist) {
+      a.ltok[(int64_t)row * a.kstride + rank] = v;
+      a.llp[(int64_t)row * a.kstride + rank] = z - lse;  // log pi
+    }
+  }
+  for (int r = klist + tid; r < a.K; r += kRowThreads) {
+    a.ltok[(int64_t)row * a.kstride + r] = -1;
+    a.llp[(int64_t)row * a.kstride + r] = neg_inf();
+  }
+  if (tid == 0) a.lse[row] = lse;
+}
+
+// ---------------------------------------------------------------------
+
+struct BestFirstArgs {
+  int B, V, n_max;
+  int klist;    // entries per list
+  int kstride;  // list row stride
+  int truncated;  // lists shorter than the rows they come from
+  const int32_t* ltok;
+  const float* llp;
+  const int32_t* ctx_len;
+  int has_cost;
+  double C_d, c0, c1, c2, c_ell;
+  int32_t *tok, *parent, *depth;
+  float* score;
+  int32_t* n_star;
+  double *phi, *thr;
+  int32_t* flag;
+  int slow;  // 0: every request, set flag when the lists are too short;
+             // 1: only flagged requests
+};
+
+// Frontier key, ascending = best-first order: (score desc, parent output
+// index asc, child rank asc).  [63:32] inverted ordered score, [31:21]
+// parent output index + 1, [20:0] child rank.
+__device__ __forceinline__ uint64_t bf_key(float s, int pout, int rank) {
+  return ((uint64_t)(~float_to_ordered(s)) << 32) |
+         ((uint64_t)(uint32_t)(pout + 1) << 21) | (uint64_t)(uint32_t)rank;
+}
+__device__ __forceinline__ int bf_pout(uint64_t k) {
+  return (int)((k >> 21) & 0x7ff) - 1;
+}
+__device__ __forceinline__ int bf_rank(uint64_t k) {
+  return (int)(k & 0x1fffff);
+}
+
+__global__ __launch_bounds__(64) void bestfirst_kernel(BestFirstArgs a) {
+  __shared__ uint64_t fkey[kFrontierCap];
+  __shared__ uint8_t fdep[kFrontierCap];
+  __shared__ float osc[1024];  // scores of the nodes taken so far
+  const int q = blockIdx.x, lane = threadIdx.x;
+  if (a.slow && !a.flag[q]) return;
+  const int B = a.B;
+  auto lrow = [&](int d) { return (int64_t)(q * B + d - 1) * a.kstride; };
+  int head = 0, tail = 0;
+
+  // insert a key keeping fkey[head..tail) ascending (one wave)
+  auto insert = [&](uint64_t key, int dep) {
+    int below = 0;
+    for (int i = head + lane; i < tail; i += kWave) below += fkey[i] < key;
+    below = wave_sum(below);
+    const int pos = head + below;
+    // shift [pos, tail) right by one, last chunk first
+    for (int c0 = ((tail - 1 - pos) / kWave) * kWave; c0 >= 0 && tail > pos;
+         c0 -= kWave) {
+      const int i = pos + c0 + lane;
+      uint64_t k = 0;
+      uint8_t dd = 0;
+      if (i < tail) {
+        k = fkey[i];
+        dd = fdep[i];
+      }
+      __builtin_amdgcn_wave_barrier();
+      if (i < tail) {
+        fkey[i + 1] = k;
+        fdep[i + 1] = dd;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    if (lane == 0) {
+      fkey[pos] = key;
+      fdep[pos] = (uint8_t)dep;
+    }
+    __builtin_amdgcn_wave_barrier();
+    ++tail;
+  };
+
+  const double ell = a.has_cost ? (double)a.ctx_len[q] : 0.0;
+  auto D = [&](double n) {
+    return a.C_d + a.c0 + a.c1 * n + a.c2 * n * n + a.c_ell * ell * n;
+  };
+  int32_t* otok = a.tok + (int64_t)q * a.n_max;
+  int32_t* opar = a.parent + (int64_t)q * a.n_max;
+  int32_t* odep = a.depth + (int64_t)q * a.n_max;
+  float* osco = a.score + (int64_t)q * a.n_max;
+
+  if (a.klist > 0) {
+    const float s = 0.0f + a.llp[lrow(1)];
+    insert(bf_key(s + 0.0f, -1, 0), 1);
+  }
+  int n = 0, overflow = 0;
+  double Phi = 0.0;
+  for (;;) {
+    if (tail == head) break;               // no prefix left
+    if (n == a.n_max) break;
+    if (!a.slow && a.truncated && n >= a.klist) {
+      overflow = 1;                        // the next head may lie past the
+      break;                               // lists: rebuild from full lists
+    }
+    if (tail + 2 > kFrontierCap) {
+      overflow = 2;
+      break;
+    }
+    const uint64_t hk = fkey[head];
+    const int hd = fdep[head];
+    const float hs = key_score(hk);
+    const double P = exp((double)hs);
+    if (a.has_cost) {
+      const double g = P * D((double)n) - (1.0 + Phi) * (D((double)n + 1.0) -
+                                                        D((double)n));
+      if (g <= 0.0) break;
+    }
+    ++head;
+    const int pout = bf_pout(hk), rank = bf_rank(hk);
+    const int htok = a.ltok[lrow(hd) + rank];
+    if (lane == 0) {
+      otok[n] = htok;
+      opar[n] = pout;
+      odep[n] = hd;
+      osco[n] = hs;
+      osc[n] = hs;
+    }
+    __builtin_amdgcn_wave_barrier();
+    Phi += P;
+    // next sibling (same parent, next rank) and first child
+    const float ps = pout < 0 ? 0.0f : osc[pout];
+    if (rank + 1 < a.klist) {
+      float s = ps + a.llp[lrow(hd) + rank + 1];
+      s = s + 0.0f;
+      insert(bf_key(s, pout, rank + 1), hd);
+    }
+    if (hd < B && a.klist > 0) {
+      float s = hs + a.llp[lrow(hd + 1)];
+      s = s + 0.0f;
+      insert(bf_key(s, n, 0), hd + 1);
+    }
+    ++n;
+  }
+  if (!a.slow) {
+    if (lane == 0) a.flag[q] = overflow;
+    if (overflow == 1) return;  // the slow pass writes this request
+  }
+  for (int i = n + lane; i < a.n_max; i += kWave) {
+    otok[i] = -1;
+    opar[i] = -1;
+    odep[i] = 0;
+    osco[i] = neg_inf();
+  }
+  if (lane == 0) {
+    a.n_star[q] = overflow == 2 ? -1 : n;
+    a.phi[q] = Phi;
+    a.thr[q] = (1.0 + Phi) / (a.has_cost ? D((double)n) : 1.0);
+  }
+}
+
+hipError_t launch_rowsel(const float* L, int rows, int V, int B, int K,
+                         int kstride, const int32_t* only_flagged, int vec_ok,
+                         float* lse, int32_t* ltok, float* llp,
+                         hipStream_t s) {
+  RowSelArgs a{L, V, B, K, kstride, only_flagged, vec_ok, lse, ltok, llp};
+  hipLaunchKernelGGL(rowsel_kernel, dim3(rows), dim3(kRowThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bestfirst(int batch, int B, int V, int n_max, int klist,
+                            int kstride, int truncated, const int32_t* ltok,
+                            const float* llp, const int32_t* ctx_len,
+                            const double* cost5, int32_t* tok,
+                            int32_t* parent, int32_t* depth, float* score,
+                            int32_t* n_star, double* phi, double* thr,
+                            int32_t* flag, int slow, hipStream_t s) {
+  BestFirstArgs a{};
+  a.B = B;
+  a.V = V;
+  a.n_max = n_max;
+  a.klist = klist;
+  a.kstride = kstride;
+  a.truncated = truncated;
+  a.ltok = ltok;
+  a.llp = llp;
+  a.ctx_len = ctx_len;
+  a.has_cost = cost5 != nullptr;
+  if (cost5) {
+    a.C_d = cost5[0];
+    a.c0 = cost5[1];
+    a.c1 = cost5[2];
+    a.c2 = cost5[3];
+    a.c_ell = cost5[4];
+  }
+  a.tok = tok;
+  a.parent = parent;
+  a.depth = depth;
+  a.score = score;
+  a.n_star = n_star;
+  a.phi = phi;
+  a.thr = thr;
+  a.flag = flag;
+  a.slow = slow;
+  hipLaunchKernelGGL(bestfirst_kernel, dim3(batch), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace pct

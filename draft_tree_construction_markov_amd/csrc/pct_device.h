@@ -127,6 +127,9 @@ __device__ __forceinline__ float wave_max(float x) {
 __device__ __forceinline__ int wave_max(int x) {
   return wave_allreduce32(x, [](int a, int b) { return a > b ? a : b; });
 }
+__device__ __forceinline__ int wave_sum(int x) {
+  return wave_allreduce32(x, [](int a, int b) { return a + b; });
+}
 __device__ __forceinline__ float wave_sum(float x) {
   return wave_allreduce32(x, [](float a, float b) { return a + b; });
 }

@@ -159,6 +159,18 @@ hipError_t launch_finalize(int P, int k, int n_slices, const float* part_c,
                            const float* gz, const int32_t* gv, int cap,
                            float* lse, int32_t* topk_tok, float* topk_logp,
                            hipStream_t s);
+hipError_t launch_rowsel(const float* L, int rows, int V, int B, int K,
+                         int kstride, const int32_t* only_flagged, int vec_ok,
+                         float* lse, int32_t* ltok, float* llp, hipStream_t s);
+hipError_t launch_bestfirst(int batch, int B, int V, int n_max, int klist,
+                            int kstride, int truncated, const int32_t* ltok,
+                            const float* llp, const int32_t* ctx_len,
+                            const double* cost5, int32_t* tok,
+                            int32_t* parent, int32_t* depth, float* score,
+                            int32_t* n_star, double* phi, double* thr,
+                            int32_t* flag, int slow, hipStream_t s);
+constexpr int kAdaptiveShortList = 64;  // list length of the first pass
+constexpr int kAdaptiveMaxNodes = 1024;
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
 hipError_t launch_mask(int batch, int N, const int32_t* parent,
                        const int32_t* n_nodes, uint64_t* mask, hipStream_t s);

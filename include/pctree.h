@@ -141,7 +141,9 @@ size_t pct_build_tree_workspace(const pct_tree_shape* shape /*host*/);
  * over a block-diffusion drafter's per-position marginals with the
  * throughput stop.  The probability of a prefix is the product of its
  * per-depth marginals, log pi_d(v) = L_d[v] - lse_d; nodes are taken in
- * best-first order, key (score desc, parent output index asc, token asc);
+ * best-first order, key (score desc, parent output index asc, child rank
+ * asc), where a child's rank orders its row by (logit desc, token asc), so
+ * equal scores fall back to the rank and equal logits to the token;
  * with P_i = exp(score_i), Phi_n = sum_{i<=n} P_i and D(n) = C(n; l), the
  * build stops at the first n whose gain
  * g(n) = P_{n+1} D(n) - (1 + Phi_n)(D(n+1) - D(n)) is not positive, i.e.
@@ -154,9 +156,16 @@ size_t pct_build_tree_workspace(const pct_tree_shape* shape /*host*/);
  *  n_star   [batch] out; phi [batch] out Phi(n*); throughput [batch] out
  *           (1 + Phi)/D(n*) (1 + Phi without a cost model)
  *  mask     [batch][n_max][ceil(n_max/64)] out, optional
- * Errors: PCT_ERR_INVALID_ARG for n_max < 1, n_max > 4096, V >= 2^18; a
- * cost model with negative c1, c2 or c_ell is rejected (the stop rule is
- * only the throughput optimum for a convex, increasing cost). */
+ * Every candidate is a child of a taken node among the min(n_max, V) best
+ * tokens of its row (a node among the n best prefixes has rank < n among
+ * its siblings), so the search is exact.  Each taken node opens at most
+ * two candidates (its next sibling and its first child), so the open set
+ * stays below 2 n_max + 2 entries.
+ * Errors: PCT_ERR_INVALID_ARG for n_max < 1, B < 1, V < 1, V >= 2^18,
+ * batch < 1 or null pointers; PCT_ERR_UNSUPPORTED for n_max > 1024 or
+ * B > 255; a cost model with negative c1, c2 or c_ell, or with
+ * C_d + c0 <= 0, is rejected (the stop rule is only the throughput optimum
+ * for a positive, convex, increasing cost). */
 pct_status pct_build_tree_adaptive(int32_t batch, int32_t B, int32_t V,
                                    int32_t n_max, const float* L,
                                    const int32_t* ctx_len,

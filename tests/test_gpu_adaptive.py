@@ -1,0 +1,113 @@
+"""GPU parity of the adaptive best-first build (pct_build_tree_adaptive)
+against the CPU oracle: the b16-sized adaptive workload (peaked and flat
+rounds, context lengths, the convex cost model), fixed budgets that need the
+full-length list pass, exhausted trees, exact ties and the closed form."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import draft_tree_construction_markov_amd as pct
+import oracle
+import synth
+from gpu_util import announce, dev_f32, dev_i32
+from treecheck import NEAR_TIE, SCORE_TOL, check_structure
+
+pytestmark = pytest.mark.gpu
+
+COST = {k: synth.ADAPTIVE[k] for k in ("C_d", "c0", "c1", "c2", "c_ell")}
+
+
+def run_compare(L, ctx, n_max, cost, label):
+    batch, B, V = L.shape
+    announce("adaptive", label, dict(batch=batch, B=B, V=V, n_max=n_max,
+                                     cost=cost is not None))
+    ab = pct.build_tree_adaptive(dev_f32(L), dev_i32(ctx), n_max, cost,
+                                 mask=True)
+    torch.cuda.synchronize()
+    g = ab.numpy()
+    bins = {"exact": 0, "near": 0}
+    for q in range(batch):
+        o = oracle.adaptive(L[q], n_max, int(ctx[q]), cost)
+        ns = int(g["n_star"][q])
+        same = (ns == o["n_star"] and
+                np.array_equal(g["tok"][q], o["tok"]) and
+                np.array_equal(g["parent"][q], o["parent"]) and
+                np.array_equal(g["depth"][q], o["depth"]))
+        if same:
+            d = np.abs(g["score"][q][:ns].astype(np.float64)
+                       - o["score"][:ns].astype(np.float64))
+            assert (d.max() if ns else 0.0) <= SCORE_TOL, q
+            assert abs(g["phi"][q] - o["phi"]) <= 1e-4 * max(1.0, o["phi"])
+            assert abs(g["throughput"][q] - o["throughput"]) <= \
+                1e-4 * o["throughput"]
+            bins["exact"] += 1
+        else:
+            near = o["min_gap"] < NEAR_TIE or o["gain_margin"] < 1e-4
+            assert near, (q, ns, o["n_star"])
+            check_structure(g["tok"][q], g["parent"][q], g["depth"][q], ns, B)
+            bins["near"] += 1
+        want = oracle.mask(g["parent"][q], max(ns, 0), n_max)
+        assert np.array_equal(g["mask"][q], want), q
+    print(f"{label}: bins {bins}, n* {list(g['n_star'][:16])}")
+    return g, bins
+
+
+def test_adaptive_workload_sample():
+    a = synth.ADAPTIVE
+    L, peaked, ctx = synth.adaptive_round(a["seed"], 16, a["B"], a["V"])
+    g, bins = run_compare(L, ctx, a["n_max"], COST, "b16-adaptive")
+    assert bins["exact"] >= 14
+
+
+def test_fixed_budget_uses_full_lists():
+    # no cost model: n* = n_max = 200 > the 64-entry first-pass lists, so the
+    # requests go through the full-length pass
+    rng = np.random.default_rng(4)
+    L = (rng.normal(size=(6, 5, 3000)) * 2).astype(np.float32)
+    ctx = np.full(6, 1000, np.int32)
+    g, bins = run_compare(L, ctx, 200, None, "fixed-200")
+    assert all(int(x) == 200 for x in g["n_star"])
+
+
+def test_exhausted_tree_and_small_vocab():
+    rng = np.random.default_rng(5)
+    L = (rng.normal(size=(3, 3, 5)) * 1.5).astype(np.float32)
+    ctx = np.full(3, 100, np.int32)
+    g, bins = run_compare(L, ctx, 300, None, "exhausted")
+    assert all(int(x) == 5 + 25 + 125 for x in g["n_star"])
+
+
+def test_uniform_rows_ties():
+    L = np.zeros((2, 4, 700), np.float32)
+    ctx = np.array([512, 30000], np.int32)
+    run_compare(L, ctx, 90, None, "uniform-fixed")
+    run_compare(L, ctx, 500, COST, "uniform-cost")
+
+
+def test_uniform_single_row_closed_form():
+    for V, ell in ((50, 0), (200, 3000), (1000, 20000)):
+        L = np.zeros((1, 1, V), np.float32)
+        ab = pct.build_tree_adaptive(dev_f32(L), dev_i32(np.array([ell])),
+                                     min(V, 1024), COST)
+        torch.cuda.synchronize()
+        c = COST
+
+        def D(n):
+            return c["C_d"] + c["c0"] + c["c1"] * n + c["c2"] * n * n + \
+                c["c_ell"] * ell * n
+        want = V
+        for n in range(V):
+            if D(n) / V <= (1 + n / V) * (D(n + 1) - D(n)):
+                want = n
+                break
+        assert int(ab.n_star[0]) == want
+
+
+def test_adaptive_rejects_bad_cost():
+    L = torch.zeros(1, 2, 100, device="cuda")
+    ctx = torch.zeros(1, dtype=torch.int32, device="cuda")
+    bad = dict(COST, c2=-1e-3)
+    with pytest.raises(pct.PCTError):
+        pct.build_tree_adaptive(L, ctx, 10, bad)
