@@ -11,9 +11,15 @@ HBM before timing starts.
 Prints one JSON line (rank 0):
   value        draft trees per second (whole job)
   roofline     the fused Markov kernel at 512 parents per launch (depths 3..16)
-               against bf16 dense MFMA peak, durations from HIP events
-               recorded around its launches inside the timed region
+               against bf16 dense MFMA peak.  Its launch durations come from
+               HIP events that the library records on the launch stream
+               around every launch, over a second pass of the same K steps
+               (so that `value` is timed without events); `traffic` is the
+               counted HBM bytes per launch from profiles/, or null when the
+               kernel changed since the counters were taken
   cpu_baseline the CPU oracle on a bounded sample of the same workload
+  adaptive     the adaptive best-first build (batch 64, n_max 1024) with its
+               row-statistics kernel against HBM peak
 """
 from __future__ import annotations
 
@@ -31,6 +37,51 @@ sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 HBM_PEAK_GBS = 8000.0
+
+
+# Kernel sources whose HBM traffic was counted (profiles/*_traffic.md); a
+# recorded figure is used only while the digest of these files still matches.
+TRAFFIC_SOURCES = {
+    "markov": ("k_markov_impl.h", "k_markov.hip", "k_markov_r16s.hip",
+               "pct_internal.h", "pct_device.h"),
+    "rowsel": ("k_adaptive.hip", "pct_internal.h", "pct_device.h"),
+}
+TRAFFIC_FILES = {"markov": "markov_topk_mfma_b16_traffic.md",
+                 "rowsel": "rowsel_adaptive_traffic.md"}
+
+
+def source_digest(kernel):
+    """sha256 of the kernel's sources with comments and blank space removed
+    (editing a comment does not change the kernel)."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "draft_tree_construction_markov_amd",
+                               "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()
+
+
+def traffic_of(kernel, launches=1):
+    """HBM bytes per launch (times `launches`) from the committed counter
+    summary, or None when the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", TRAFFIC_FILES[kernel])
+    try:
+        fields = {}
+        for line in open(path):
+            if ":" in line and line.split(":", 1)[0] in (
+                    "source_digest", "traffic_bytes_per_launch"):
+                k, v = line.split(":", 1)
+                fields[k] = v.strip().strip("`")
+        if fields.get("source_digest") != source_digest(kernel):
+            return None
+        return float(fields["traffic_bytes_per_launch"]) * launches
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def log(*a):
@@ -154,7 +205,7 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 1),
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": None,
+                "traffic": traffic_of("markov"),
                 "kernel": "markov_topk_mfma<2,8,16> (512 parents/launch)",
                 "avg_launch_ms": round(k1_avg_ms, 5),
                 "launches": k1_n}
@@ -205,20 +256,27 @@ def bench_adaptive(args, pct, synth, torch, dev):
     for _ in range(args.warmup):
         ab.run(dL, dC)
     torch.cuda.synchronize()
-    pct.profile_reset()
-    pct.profile_enable(True)
     t1 = time.perf_counter()
     for _ in range(args.steps):
         ab.run(dL, dC)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t1) * 1e3 / args.steps
+    # the same steps again with per-launch events: the row-statistics time
+    # of a step is every row-statistics launch in it (the full-length pass
+    # only touches rows of requests that outgrew the short lists)
+    pct.profile_reset()
+    pct.profile_enable(True)
+    for _ in range(args.steps):
+        ab.run(dL, dC)
+    torch.cuda.synchronize()
     pct.profile_enable(False)
     rs_ms, rs_n = pct.profile_read(pct.PROF_ROWSTATS, -1)
+    bf_ms, _ = pct.profile_read(pct.PROF_BESTFIRST, -1)
     pct.profile_reset()
     ns = ab.n_star.cpu().numpy()
     bytes_rows = float(L.nbytes)
-    rs_avg = rs_ms / max(rs_n, 1)
-    gbs = bytes_rows / (rs_avg * 1e-3) / 1e9
+    rs_step = rs_ms / args.steps
+    gbs = bytes_rows / (rs_step * 1e-3) / 1e9
     return {"workload": "adaptive: batch 64, V=151936, B=16, n_max=1024, "
                         "marginal rows, half peaked / half flat",
             "trees_per_sec": round(a["batch"] / (ms / 1e3), 1),
@@ -228,8 +286,11 @@ def bench_adaptive(args, pct, synth, torch, dev):
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4),
-                         "traffic": None, "kernel": "row statistics",
-                         "avg_launch_ms": round(rs_avg, 5)}}
+                         "traffic": traffic_of("rowsel"),  # per step
+                         "kernel": "rowsel_kernel (1024 rows/step)",
+                         "ms_per_step": round(rs_step, 5),
+                         "launches_per_step": rs_n // args.steps},
+            "bestfirst_ms_per_step": round(bf_ms / args.steps, 5)}
 
 
 def cpu_baseline(args, w, L, U, W, A):

@@ -1,7 +1,7 @@
 // k_markov.hip -- planning and dispatch of the fused Markov-logit kernel
 // (the MFMA kernel itself is in k_markov_impl.h), and its plain VALU variant.
 // The fused Markov-logit kernel of the parent-conditioned
-// tree (PCTree article, "chain -> tree": z_d(p) = L_d + Markov(p) for every
+// tree (PCTree article, "straight draft": z_d(p) = L_d + Markov(p) for every
 // frontier parent in one batched call, then each parent's log-softmax and
 // local top-k).
 //

@@ -1,5 +1,5 @@
 // k_markov_impl.h -- the fused Markov-logit kernel of the parent-conditioned
-// tree (PCTree article, "chain -> tree": z_d(p) = L_d + Markov(p) for every
+// tree (PCTree article, "straight draft": z_d(p) = L_d + Markov(p) for every
 // frontier parent in one batched call, then each parent's log-softmax and
 // local top-k).
 //

@@ -1,5 +1,5 @@
 // k_select.hip -- per-request selection kernels of the parent-conditioned
-// tree (PCTree article, "chain -> tree"): merging the per-slice partials of
+// tree (PCTree article, "straight draft"): merging the per-slice partials of
 // the fused Markov kernel into each parent's log-normaliser and local top-k,
 // path scores s(c) = s(p) + log pi(c|p), the per-depth beam (top-k pruning
 // at each stage), and the global top-N that fits the verify budget.  Also

@@ -1,6 +1,6 @@
 // k_verify.hip -- checking a draft tree: the packed ancestry mask that lets
-// the target verify the whole tree in one forward (PCTree article, "chain ->
-// tree"), and the greedy acceptance walk (DSpark explainer, "one inference,
+// the target verify the whole tree in one forward (PCTree article, "straight
+// draft"), and the greedy acceptance walk (DSpark explainer, "one inference,
 // from guess to confirmation": keep the run of matches from the root, stop at
 // the first mismatch, where the target supplies its own token).
 #include "pct_device.h"

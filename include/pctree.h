@@ -4,8 +4,9 @@
  *
  * Pages the operations come from (cited by title and section):
  *  [PCT] qiita article on PCTree (Parent-Conditioned Drafting Tree),
- *        sections "DSpark" and "a straight draft loses everything after the
- *        first miss" (chain -> tree).
+ *        section "a straight draft is wasted once its first token misses"
+ *        (cited below as "straight draft"): DSpark's Markov head
+ *        z_d = L_d + Markov(y_{d-1}) and the chain -> tree step.
  *  [DSP] DSpark / DeepSeek-V4 explainer (xiaohu-jiedu), section "one
  *        inference, from guess to confirmation".
  *  [CAD] "Cost-Aware Diffusion Draft Trees for Speculative Decoding"
@@ -73,7 +74,7 @@ typedef struct {
 } pct_cost_model;
 
 /* ------------------------------------------------------------------------
- * pct_markov_logits -- [PCT] "DSpark" and "chain -> tree": for P parents
+ * pct_markov_logits -- [PCT] "straight draft": for P parents
  * at once, z_p = L[row_p] + Markov(tok_p) with Markov(t)[v] = U[t] . W[v],
  * then the log-softmax normaliser of z_p over the vocabulary and its top-k.
  *
@@ -104,7 +105,7 @@ pct_status pct_markov_logits(const float* L, int64_t L_row_stride,
 size_t pct_markov_logits_workspace(int32_t P, int32_t V, int32_t k);
 
 /* ------------------------------------------------------------------------
- * pct_build_tree -- [PCT] "chain -> tree": the parent-conditioned draft tree.
+ * pct_build_tree -- [PCT] "straight draft": the parent-conditioned draft tree.
  * Depth d = 1..B expands every frontier parent p with
  * z_d(p) = L_d + Markov(p) (one batched call per depth), keeps each
  * parent's top-k children by log pi(v|p) = z - lse, scores a child by its
@@ -180,7 +181,7 @@ size_t pct_build_tree_adaptive_workspace(int32_t batch, int32_t B, int32_t V,
                                          int32_t n_max);
 
 /* ------------------------------------------------------------------------
- * pct_tree_mask -- [PCT] "chain -> tree": the whole tree is verified in one
+ * pct_tree_mask -- [PCT] "straight draft": the whole tree is verified in one
  * target forward, in which a node may see only itself and its ancestors.
  *  parent  [batch][N] (-1 = root), n_nodes [batch]
  *  mask    [batch][N][ceil(N/64)] out; rows >= n_nodes are zero

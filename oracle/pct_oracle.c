@@ -32,7 +32,7 @@ static double factor_at(const void* p, int32_t dtype, int64_t i) {
   return (double)((const float*)p)[i];
 }
 
-/* [PCT] "DSpark": the Markov head adds a term that depends on the previous
+/* [PCT] "straight draft": the Markov head adds a term that depends on the previous
  * token only.  Stand-in: Markov(t)[v] = sum_j U[t][j] W[v][j]. */
 int ref_markov_row(const void* U, const void* W, int32_t uw_dtype, int32_t V,
                    int32_t r, int32_t tok, float* out) {
@@ -65,7 +65,7 @@ static int cmp_zv(const void* a, const void* b) {
   return (x->v > y->v) - (x->v < y->v);
 }
 
-/* [PCT] "chain -> tree": pi(.|p) is the softmax of z_d(p) = L_d + Markov(p);
+/* [PCT] "straight draft": pi(.|p) is the softmax of z_d(p) = L_d + Markov(p);
  * each parent keeps its local top-k children. */
 int ref_row_stats(const float* Lrow, const float* Mrow, int32_t V, int32_t k,
                   float* lse, int32_t* topk_tok, float* topk_z,
@@ -143,7 +143,7 @@ static void gap_update(double* g, float a, float b) {
   if (d < *g) *g = d;
 }
 
-/* [PCT] "chain -> tree", in the article's order: for every frontier parent
+/* [PCT] "straight draft", in the article's order: for every frontier parent
  * p compute z_d(p) = L_d + Markov(p) (one call for the whole frontier), take
  * the per-parent log-softmax and local top-k, score every child by its path
  * log-probability s(c) = s(p) + log pi(c|p), prune each stage to the beam,
@@ -273,7 +273,7 @@ int ref_build_tree(const ref_tree_shape* sh, const float* L, const void* U,
   return rc;
 }
 
-/* [PCT] "DSpark": the chain drafter picks, at every position, the most
+/* [PCT] "straight draft": the chain drafter picks, at every position, the most
  * probable token given the previous one. */
 int ref_greedy_chain(int32_t B, int32_t V, int32_t r, const float* L,
                      const void* U, const void* W, int32_t uw_dtype,
@@ -552,7 +552,7 @@ int ref_adaptive(int32_t B, int32_t V, int32_t n_max, const float* L,
 /* ------------------------------------------------------------------ */
 /* verification                                                         */
 
-/* [PCT] "chain -> tree": the whole tree is checked in one target forward;
+/* [PCT] "straight draft": the whole tree is checked in one target forward;
  * each node may attend to itself and its ancestors only. */
 void ref_mask(int32_t N, int32_t n_nodes, const int32_t* parent,
               uint64_t* mask) {
@@ -566,7 +566,7 @@ void ref_mask(int32_t N, int32_t n_nodes, const int32_t* parent,
   }
 }
 
-/* [DSP] "one cycle of inference": walk from the root, accept the child whose
+/* [DSP] "one inference, from guess to confirmation": walk from the root, accept the child whose
  * token equals the target's choice, stop at the first mismatch; the target's
  * own token there is the bonus.  tau counts accepted tokens plus the bonus. */
 int ref_accept(int32_t N, int32_t n_nodes, int32_t B, const int32_t* tok,

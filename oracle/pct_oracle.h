@@ -8,13 +8,16 @@
  * It shares no code, header, table or helper with the GPU library.
  *
  * Sources (cited by page title and section):
- *  [PCT]  "PCTree" practitioner article on qiita (okssusucha), sections
- *         "DSpark" (Markov head z_d = L_d + Markov(y_{d-1})) and
- *         "chain -> tree" (z_d(p) = L_d + Markov(p) for all frontier parents,
+ *  [PCT]  "PCTree" practitioner article on qiita (okssusucha), section
+ *         "a straight draft is wasted once its first token misses" (cited
+ *         as "straight draft"): the Markov head z_d = L_d + Markov(y_{d-1})
+ *         and the chain -> tree step (z_d(p) = L_d + Markov(p) for all
+ *         frontier parents,
  *         per-parent log-softmax and local top-k, path score
  *         s(c) = sum log pi(v|u), top-k pruning per stage, global top-N under
  *         the verify budget, one verification forward over the tree).
- *  [DSP]  DSpark explainer (xiaohu-jiedu), section "one cycle of inference":
+ *  [DSP]  DSpark explainer (xiaohu-jiedu), section "one inference, from guess to
+ *         confirmation":
  *         compare in order, keep consecutive matches, stop at the first
  *         mismatch, the target supplies its own token there (bonus); worked
  *         example of 4 accepted + 1 corrected token.
