@@ -234,6 +234,38 @@ __device__ void wave_topk(const float* gz, const int32_t* gv, int cnt, int k,
   }
 }
 
+// The k best candidates (z desc, token asc) of a parent, one wave: with at
+// most 64 candidates every lane takes one and counts the candidates that
+// come before it (read back from the wave's LDS scratch, 64 float2), so the
+// k results come out in one pass; emit(i, z, v) is called by the lane that
+// holds result i.  Missing results (fewer than k candidates, which a valid
+// seed rules out) are emitted by lane 0 as (-inf, 0).  More than 64
+// candidates take k passes of wave-wide arg-max.
+template <typename F>
+__device__ void wave_topk_rank(const float* gz, const int32_t* gv, int cnt,
+                               int k, int lane, float2* scratch, F&& emit) {
+  if (cnt > kWave) {
+    wave_topk(gz, gv, cnt, k, lane, [&](int i, float z, int32_t v) {
+      if (lane == 0) emit(i, z, v);
+    });
+    return;
+  }
+  const float cz = lane < cnt ? gz[lane] : neg_inf();
+  const int32_t cv = lane < cnt ? gv[lane] : 0x7fffffff;
+  scratch[lane] = make_float2(cz, __int_as_float(cv));
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  int rank = 0;
+  for (int o = 0; o < cnt; ++o) {
+    const float2 e = scratch[o];
+    rank += zv_before(e.x, __float_as_int(e.y), cz, cv);
+  }
+  if (lane < cnt && rank < k) emit(rank, cz, cv);
+  if (lane == 0)
+    for (int i = cnt; i < k; ++i) emit(i, neg_inf(), 0);
+}
+
 // Seeds of up to 32 parents that share one L row (one wave), computed with
 // the same bf16 MFMA as the fused kernel: the seed tokens form the 32 "vocab"
 // rows of a 32x32x16 block and the parents its columns.  A second MFMA on
@@ -375,86 +407,271 @@ __global__ __launch_bounds__(64) void init_kernel(int B, const int32_t* anchor,
   }
 }
 
+// Seed threshold of one parent (one wave) from LDS operands: the W rows
+// of the kSeedT seed tokens (wrows, r/8 + 1 16-byte chunks per row),
+// their logits lval and tokens vt (-1 = none), and the parent's U row (urow,
+// r/8 chunks).  Lane l takes seed token l%32 and half l/32 of the rank
+// dimension; the fp32 dot products differ from the fused kernel's MFMA sums
+// of the same exact products by less than the margin.  scratch: kSeedT
+// floats of LDS private to the wave.
+__device__ float seed_theta_lds(const SeedArgs& sa, const uint4* wrows,
+                                const uint4* urow, const float* lval,
+                                const int* vt, int lane, float* scratch) {
+  const int t = lane & 31, h = lane >> 5;
+  const int half = sa.r / 16;  // chunks per half of the rank dimension
+  const int cs = sa.r / 8 + 1;  // W row stride in chunks (one pad chunk)
+  // four independent partial sums keep the dependent chains short
+  float acc[4] = {0.f, 0.f, 0.f, 0.f}, aa[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int c = h * half; c < (h + 1) * half; ++c) {
+    const uint4 a4 = urow[c], b4 = wrows[t * cs + c];
+    const uint32_t ua[4] = {a4.x, a4.y, a4.z, a4.w};
+    const uint32_t wb[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float u0 = __uint_as_float(ua[i] << 16);
+      const float u1 = __uint_as_float(ua[i] & 0xffff0000u);
+      const float w0 = __uint_as_float(wb[i] << 16);
+      const float w1 = __uint_as_float(wb[i] & 0xffff0000u);
+      acc[i] = fmaf(u0, w0, acc[i]);
+      aa[i] += fabsf(u0 * w0);
+      acc[i] = fmaf(u1, w1, acc[i]);
+      aa[i] += fabsf(u1 * w1);
+    }
+  }
+  const float m4 = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  const float a4s = (aa[0] + aa[1]) + (aa[2] + aa[3]);
+  const float m = m4 + swap_halves(m4, lane);
+  const float A = a4s + swap_halves(a4s, lane);
+  const bool ok = h == 0 && vt[t] >= 0;
+  const float z = ok ? lval[t] + m : neg_inf();
+  const float Amax = wave_max(ok ? A : 0.f);
+  const float zmax = wave_max(ok ? fabsf(z) : 0.f);
+  // the k-th largest z: the value whose rank (ties by seed slot) is k-1
+  if (h == 0) scratch[t] = z;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  int rank = 0;
+  for (int o = 0; o < kSeedT; ++o) {
+    const float zo = scratch[o];
+    rank += zo > z || (zo == z && o < t);
+  }
+  const float kth = wave_max(h == 0 && rank == sa.k - 1 ? z : neg_inf());
+  const float margin = 4.f * (float)sa.r * 5.9604645e-8f * Amax +
+                       4.f * 1.1920929e-7f * zmax + 1e-30f;
+  return kth - margin;
+}
+
+// The log-normaliser of one parent from its (c, s) partials, one wave:
+// part(i) returns partial i of S.  Each lane keeps a running (max, sum) with
+// a double sum; lanes combine by DPP reductions.
+template <typename F>
+__device__ float wave_lse_from(F&& part, int S, int lane) {
+  float cm = neg_inf();
+  double acc = 0.0;
+  for (int i = lane; i < S; i += kWave) {
+    const float2 cv = part(i);
+    if (cv.x == neg_inf() || !(cv.y > 0.f)) continue;
+    if (cv.x > cm) {
+      acc = acc * (double)__builtin_amdgcn_exp2f(cm - cv.x) + (double)cv.y;
+      cm = cv.x;
+    } else {
+      acc += (double)cv.y * (double)__builtin_amdgcn_exp2f(cv.x - cm);
+    }
+  }
+  const float gm = wave_max(cm);
+  acc = (cm == neg_inf()) ? 0.0
+                          : acc * (double)__builtin_amdgcn_exp2f(cm - gm);
+  acc = wave_sum(acc);
+  return (float)(kLn2 * ((double)gm + log2(acc)));
+}
+
 // One workgroup per request: children of every frontier parent, their
 // scores and pool keys, the beam of the next depth and its seeds.
+//  1. all independent loads first: the next row's seed tokens, their logits
+//     and W rows; the partials of up to 16 parents, read coalesced ([S][P]
+//     rows of consecutive parents) into LDS;
+//  2. one wave per parent: log-normaliser and top-k of its candidates;
+//  3. the U rows of every child are prefetched to LDS (direct global->LDS
+//     loads) while the beam (rank of each child's key) is computed;
+//  4. one wave per new parent: its seed threshold for the next depth.
 constexpr int kExpandWaves = 16;
+constexpr int kStageSlices = 256;  // partials per parent staged in LDS
+constexpr int kUPre = 128;         // children whose U rows are prefetched
 __global__ __launch_bounds__(kExpandWaves * 64) void expand_kernel(
     ExpandArgs a) {
   __shared__ uint64_t ckey[kMaxCand];
   __shared__ int32_t cpid[kMaxCand];
-  __shared__ int32_t ntok[kMaxCand];
+  __shared__ int32_t ctok[kMaxCand];
+  __shared__ int32_t crank[kMaxCand];
+  __shared__ float2 pst[kExpandWaves * kStageSlices];
+  // child index of each beam rank (the partials are consumed by then)
+  int32_t* bcand = reinterpret_cast<int32_t*>(pst);
+  static_assert(sizeof(pst) >= (kMaxCand + kExpandWaves * kSeedT) * 4,
+                "beam indices and seed scratch");
   __shared__ uint4 wrows[kSeedT * kSeedRowChunks];
-  __shared__ uint4 urows[32 * kSeedRowChunks];
+  __shared__ uint4 upre[kUPre * 32];  // U rows (r <= 256: 32 chunks each)
   __shared__ float lval[kSeedT];
   __shared__ int vt[kSeedT];
+  constexpr int NT = kExpandWaves * 64;
   const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63,
             wave = tid >> 6;
   const int NC = a.Fp * a.k;
   const int row = q * a.B + a.d;  // L row of depth d+1
-  const bool mseed = a.d < a.B && seed_by_mfma(a.seed);
-  // the next depth's seed tokens are known already: stage their W rows and
-  // logits now, overlapping the merge below
-  if (mseed)
-    stage_seed_rows(a.seed, row, wrows, lval, vt, tid, kExpandWaves * 64);
-  for (int j = wave; j < a.Fp; j += kExpandWaves) {
-    const int p = q * a.Fp + j;
-    const int sp = a.shared_stats ? q : p;
-    const float sp_score = a.cur.s[p];
-    const int ppid = a.cur.pid[p];
-    const int cnt = min(a.gcnt[sp], a.cap);
-    const float lse =
-        wave_merge_lse(a.part_c, a.part_s, a.n_slices, a.Pstat, sp, lane);
-    wave_topk(a.gz + (int64_t)sp * a.cap, a.gv + (int64_t)sp * a.cap, cnt,
-              a.k, lane, [&](int i, float z, int32_t v) {
-                if (lane == 0) {
-                  const float l = z - lse;       // log pi(v|p)
-                  float s = sp_score + l;        // path score
-                  s = s + 0.0f;                  // -0 -> +0
-                  const int pid = a.base_d + j * a.k + i;
-                  const uint64_t key = make_key(s, ppid, v);
-                  ckey[j * a.k + i] = key;
-                  cpid[j * a.k + i] = pid;
-                  a.pool_key[(int64_t)q * a.pool_n + pid] = key;
-                }
-              });
-  }
-  __syncthreads();
-  // beam: the Fn smallest keys of this depth's children (keys are
-  // distinct: (parent, token) pairs are unique)
-  auto emit_beam = [&](int rank, uint64_t key, int pid) {
-    const int o = q * a.Fn + rank;
-    a.nxt.tok[o] = key_tok(key);
-    a.nxt.pid[o] = pid;
-    a.nxt.s[o] = key_score(key);
-    a.nxt.lrow[o] = q * a.B + a.d;  // row of depth d+1
-    ntok[rank] = key_tok(key);
-    if (a.gcnt_next) a.gcnt_next[o] = 0;
-  };
-  for (int c = tid; c < NC; c += kExpandWaves * 64) {
-    const uint64_t key = ckey[c];
-    int rank = 0;
-    for (int o = 0; o < NC; ++o) rank += ckey[o] < key;
-    if (rank < a.Fn) emit_beam(rank, key, cpid[c]);
-  }
-  if (a.d >= a.B) return;
-  __syncthreads();
-  if (mseed) {
-    for (int base = 0; base < a.Fn; base += 32) {
-      const int np = min(32, a.Fn - base);
-      stage_parent_rows(a.seed, ntok + base, np, urows, tid,
-                        kExpandWaves * 64);
-      __syncthreads();
-      if (wave == 0) {
-        const float th = seed_theta_mfma(a.seed, wrows, urows, lval, vt, lane);
-        if (lane < np) a.nxt.theta[q * a.Fn + base + lane] = th;
+  const bool lseed = a.d < a.B && seed_by_mfma(a.seed);  // bf16, r <= 256
+  const int ch = a.seed.r / 8;
+  const bool staged = !a.shared_stats && a.n_slices <= kStageSlices;
+  const bool upref = lseed && NC <= kUPre;
+  // partials of a group of up to 16 parents into LDS; the first group's
+  // loads are issued before the seed staging so that the two overlap
+  constexpr int kStageIt = kExpandWaves * kStageSlices / NT;
+  float2 pre[kStageIt];
+  auto load_group = [&](int g0) {
+    const int ng = min(kExpandWaves, a.Fp - g0);
+    const int p0 = q * a.Fp + g0, S = a.n_slices;
+#pragma unroll
+    for (int it = 0; it < kStageIt; ++it) {
+      const int e = tid + it * NT;
+      pre[it] = make_float2(neg_inf(), 0.f);
+      if (e < S * ng) {
+        const int64_t o = (int64_t)(e / ng) * a.Pstat + p0 + e % ng;
+        pre[it] = make_float2(a.part_c[o], a.part_s[o]);
       }
+    }
+  };
+  auto store_group = [&](int g0) {
+    const int ng = min(kExpandWaves, a.Fp - g0), S = a.n_slices;
+#pragma unroll
+    for (int it = 0; it < kStageIt; ++it) {
+      const int e = tid + it * NT;
+      if (e < S * ng) pst[(e % ng) * kStageSlices + e / ng] = pre[it];
+    }
+  };
+  if (staged) load_group(0);
+  if (lseed)
+    stage_seed_rows(a.seed, row, wrows, lval, vt, tid, NT);
+  for (int i = tid; i < NC; i += NT) crank[i] = 0;
+
+  for (int g0 = 0; g0 < a.Fp; g0 += kExpandWaves) {
+    const int ng = min(kExpandWaves, a.Fp - g0);
+    if (staged) {
+      if (g0 > 0) {
+        __syncthreads();  // the previous group is consumed
+        load_group(g0);
+      }
+      store_group(g0);
       __syncthreads();
+    }
+    const int j = g0 + wave;
+    if (wave < ng) {
+      const int p = q * a.Fp + j;
+      const int sp = a.shared_stats ? q : p;
+      const float sp_score = a.cur.s[p];
+      const int ppid = a.cur.pid[p];
+      const int cnt = min(a.gcnt[sp], a.cap);
+      float lse;
+      if (staged) {
+        const float2* pp = pst + wave * kStageSlices;
+        lse = wave_lse_from([&](int i) { return pp[i]; }, a.n_slices, lane);
+      } else {
+        lse = wave_lse_from(
+            [&](int i) {
+              const int64_t o = (int64_t)i * a.Pstat + sp;
+              return make_float2(a.part_c[o], a.part_s[o]);
+            },
+            a.n_slices, lane);
+      }
+      // the wave's partials are consumed: its LDS rows serve as scratch
+      wave_topk_rank(a.gz + (int64_t)sp * a.cap, a.gv + (int64_t)sp * a.cap,
+                     cnt, a.k, lane, pst + wave * kStageSlices,
+                     [&](int i, float z, int32_t v) {
+                       const float l = z - lse;       // log pi(v|p)
+                       float s = sp_score + l;        // path score
+                       s = s + 0.0f;                  // -0 -> +0
+                       const int c = j * a.k + i;
+                       const int pid = a.base_d + c;
+                       const uint64_t key = make_key(s, ppid, v);
+                       ckey[c] = key;
+                       cpid[c] = pid;
+                       ctok[c] = v;
+                       a.pool_key[(int64_t)q * a.pool_n + pid] = key;
+                     });
+    }
+  }
+  __syncthreads();
+
+  // U rows of every child, in flight while the beam is ranked
+  if (upref) {
+    const uint4* Ug = reinterpret_cast<const uint4*>(a.seed.U);
+    for (int i0 = wave * 64; i0 < NC * ch; i0 += NT) {
+      const int i = min(i0 + lane, NC * ch - 1);
+      const int c = i / ch, cc = i % ch;
+      const int tok = min(max(ctok[c], 0), a.seed.V - 1);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(Ug +
+                                                          (int64_t)tok * ch +
+                                                          cc),
+          (__attribute__((address_space(3))) void*)(upre + i0), 16, 0, 0);
+    }
+  }
+  // beam: the Fn smallest keys of this depth's children (keys are distinct:
+  // (parent, token) pairs are unique); rank counts split over the threads
+  const int parts = NC <= NT ? max(1, NT / NC) : 1;
+  if (NC <= NT) {
+    const int c = tid % NC, part = tid / NC;
+    if (part < parts) {
+      const uint64_t key = ckey[c];
+      const int o0 = (int)((int64_t)NC * part / parts);
+      const int o1 = (int)((int64_t)NC * (part + 1) / parts);
+      int r = 0;
+      for (int o = o0; o < o1; ++o) r += ckey[o] < key;
+      atomicAdd(&crank[c], r);
     }
   } else {
-    for (int i = wave; i < a.Fn; i += kExpandWaves) {
-      const float th = seed_theta(a.seed, ntok[i], row, lane);
-      if (lane == 0) a.nxt.theta[q * a.Fn + i] = th;
+    for (int c = tid; c < NC; c += NT) {
+      const uint64_t key = ckey[c];
+      int r = 0;
+      for (int o = 0; o < NC; ++o) r += ckey[o] < key;
+      crank[c] = r;
     }
+  }
+  __syncthreads();
+  for (int c = tid; c < NC; c += NT) {
+    const int rank = crank[c];
+    if (rank < a.Fn) {
+      const uint64_t key = ckey[c];
+      const int o = q * a.Fn + rank;
+      a.nxt.tok[o] = key_tok(key);
+      a.nxt.pid[o] = cpid[c];
+      a.nxt.s[o] = key_score(key);
+      a.nxt.lrow[o] = row;  // row of depth d+1
+      bcand[rank] = c;
+      if (a.gcnt_next) a.gcnt_next[o] = 0;
+    }
+  }
+  if (a.d >= a.B) return;
+  if (upref) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // seeds of the next depth's parents, one wave each
+  for (int i = wave; i < a.Fn; i += kExpandWaves) {
+    float th;
+    if (lseed) {
+      const int c = bcand[i];
+      const uint4* urow;
+      if (upref) {
+        urow = upre + c * ch;
+      } else {
+        urow = reinterpret_cast<const uint4*>(a.seed.U) +
+               (int64_t)min(max(ctok[c], 0), a.seed.V - 1) * ch;
+      }
+      // wave scratch after the beam indices (kMaxCand ints) in pst
+      float* scr = reinterpret_cast<float*>(pst) + kMaxCand + wave * kSeedT;
+      th = seed_theta_lds(a.seed, wrows, urow, lval, vt, lane, scr);
+    } else {
+      th = seed_theta(a.seed, ctok[bcand[i]], row, lane);
+    }
+    if (lane == 0) a.nxt.theta[q * a.Fn + i] = th;
   }
 }
 

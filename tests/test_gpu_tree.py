@@ -102,6 +102,19 @@ def test_markov_tree_parity(batch, B, V, k, beam, N, r):
     run_and_compare(L, U, W, A, k, beam, N)
 
 
+@pytest.mark.parametrize("batch,B,V,k,beam,N,r,reqs", [
+    # frontiers above 256 parents take the ping-pong kernel: two parent
+    # tiles, one 32-row sub-tile per slice (tail steps), ragged last tile
+    (40, 3, 3000, 8, 16, 64, 256, None),
+    (36, 4, 5000, 8, 16, 96, 128, None),          # rank 128
+    (33, 3, 2002, 8, 16, 64, 256, None),          # V % 4 != 0: other kernel
+    (24, 3, 151936, 8, 16, 64, 256, [0, 11, 23]),  # full vocabulary
+])
+def test_large_frontier_parity(batch, B, V, k, beam, N, r, reqs):
+    L, U, W, A = _random(batch * 7 + V, batch, B, V, r)
+    run_and_compare(L, U, W, A, k, beam, N, reqs=reqs)
+
+
 def test_marginal_tree_parity():
     L, U, W, A = _random(7, 5, 6, 5000, 0)
     run_and_compare(L, U, W, A, 8, 16, 128)
