@@ -170,6 +170,36 @@ def test_b16_workload_sampled():
         assert np.all(sc[:-1] >= sc[1:])
 
 
+def test_round_workload_sampled():
+    # the full round at its own size (batch 128, N = 512, 512x512 masks,
+    # acceptance walk): three requests through the oracle, every tree
+    # through the structural checks, every walk against the oracle's walk
+    w = synth.TREE_WORKLOADS["round"]
+    print("generating the round inputs (1.2 GB of logits)", flush=True)
+    L, U, W, A = synth.tree_inputs(w)
+    g, o, bins = run_and_compare(L, U, W, A, w.k, w.beam_w, w.N,
+                                 reqs=[0, 77, 127])
+    for q in range(w.batch):
+        n = int(g["n_nodes"][q])
+        assert n == w.N
+        check_structure(g["tok"][q], g["parent"][q], g["depth"][q], n, w.B)
+        sc = g["score"][q]
+        assert np.all(sc[:-1] >= sc[1:])
+    tgt = synth.targets_from_tree(w.seed, g["tok"], g["parent"], g["depth"],
+                                  g["n_nodes"], A, w.V, w.B,
+                                  synth.round_agreement(w.B))
+    announce("round verify", dict(batch=w.batch, N=w.N))
+    tau, an, at = pct.verify_accept(dev_i32(g["tok"]), dev_i32(g["parent"]),
+                                    dev_i32(g["depth"]), dev_i32(g["n_nodes"]),
+                                    dev_i32(tgt), w.B)
+    tau, an, at = tau.cpu().numpy(), an.cpu().numpy(), at.cpu().numpy()
+    for q in range(w.batch):
+        t2, an2, at2 = oracle.accept(g["tok"][q], g["parent"][q],
+                                     int(g["n_nodes"][q]), w.B, tgt[q])
+        assert tau[q] == t2 and list(an[q]) == list(an2) and \
+            list(at[q]) == list(at2), q
+
+
 def test_verify_standalone_matches_oracle():
     # the walk on identical inputs (oracle trees and synthetic targets)
     # must match bit for bit
