@@ -456,6 +456,11 @@ struct AdaptiveWs {
   float* lse_s;
   int32_t* ltok_s;
   float* llp_s;
+  // pieces of the single-read short-list pass
+  float* pm;
+  double* ps;
+  float* cz;
+  int32_t* cv;
 };
 size_t carve_adaptive(int batch, int B, int V, int n_max, void* ws,
                       AdaptiveWs& w, int& Kf, int& Ks) {
@@ -470,6 +475,11 @@ size_t carve_adaptive(int batch, int B, int V, int n_max, void* ws,
   w.lse_s = c.take<float>(rows);
   w.ltok_s = c.take<int32_t>(rows * Ks);
   w.llp_s = c.take<float>(rows * Ks);
+  const int64_t pieces = rows * rowpart_pieces(V);
+  w.pm = c.take<float>(pieces);
+  w.ps = c.take<double>(pieces);
+  w.cz = c.take<float>(pieces * Kf);
+  w.cv = c.take<int32_t>(pieces * Kf);
   return c.off;
 }
 pct_status check_adaptive(int32_t batch, int32_t B, int32_t V, int32_t n_max) {
@@ -536,8 +546,12 @@ pct_status pct_build_tree_adaptive(int32_t batch, int32_t B, int32_t V,
   hipError_t e;
   {
     ProfScope ps(PROF_ROWSTATS, rows, s);
-    e = launch_rowsel(L, rows, V, B, Kf, Kf, nullptr, vec_ok, w.lse_f,
-                      w.ltok_f, w.llp_f, s);
+    if (rowpart_ok(V, Kf, vec_ok))
+      e = launch_rowpart(L, rows, V, Kf, Kf, w.pm, w.ps, w.cz, w.cv, w.lse_f,
+                         w.ltok_f, w.llp_f, s);
+    else
+      e = launch_rowsel(L, rows, V, B, Kf, Kf, nullptr, vec_ok, w.lse_f,
+                        w.ltok_f, w.llp_f, s);
   }
   if (e != hipSuccess) return hip_fail(e, "row statistics kernel");
   {

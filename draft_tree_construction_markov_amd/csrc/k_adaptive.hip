@@ -24,6 +24,9 @@ namespace pct {
 constexpr int kRowThreads = 1024;
 constexpr int kRowCap = 4096;       // LDS candidate buffer of rowsel
 constexpr int kFrontierCap = 4096;  // LDS frontier of bestfirst
+constexpr int kPartThreads = 512;  // single-read row statistics
+constexpr int kPartVec = 19;       // 16-byte loads per thread
+constexpr int kPartCap = 2048;     // LDS candidate buffer of rowpart
 
 struct RowSelArgs {
   const float* L;
@@ -33,6 +36,26 @@ struct RowSelArgs {
   float* lse;     // [rows]
   int32_t* ltok;  // [rows][kstride]
   float* llp;     // [rows][kstride]  log pi = fp32(L - lse)
+};
+
+// Single-read row statistics (see rowpart_kernel).
+struct RowPartArgs {
+  const float* L;
+  int V, K, parts, chunk4;  // chunk4: 16-byte vectors per piece
+  float* pm;    // [rows][parts] piece maximum, log2 units
+  double* ps;   // [rows][parts] piece sum of 2^(z log2e - pm)
+  float* cz;    // [rows][parts][K] piece best K, sorted; padding (-inf,
+  int32_t* cv;  //   INT32_MAX)
+};
+struct RowMergeArgs {
+  int K, parts, kstride;
+  const float* pm;
+  const double* ps;
+  const float* cz;
+  const int32_t* cv;
+  float* lse;
+  int32_t* ltok;
+  float* llp;
 };
 
 __device__ __forceinline__ bool not_after(float z, int v, float tz, int tv) {
@@ -238,6 +261,292 @@ __global__ __launch_bounds__(kRowThreads) void rowsel_kernel(RowSelArgs a) {
 }
 
 // ---------------------------------------------------------------------
+// Single-read row statistics for short lists.  A row is cut into `parts`
+// contiguous pieces; one workgroup per piece holds its piece in registers
+// (at most kPartVec 16-byte loads per thread), so every logit is read from
+// memory once.  A piece yields its maximum, its sum of exponentials relative
+// to that maximum and its exact best K (logit desc, token asc), sorted.  The
+// row's best K lie in the union of its pieces' best K, which the merge
+// kernel ranks with one binary search per other piece.
+
+__device__ __forceinline__ uint64_t zv_key(float z, int v) {
+  // larger key = earlier in (logit desc, token asc)
+  return ((uint64_t)float_to_ordered(z) << 32) | (uint32_t)(0x7fffffff - v);
+}
+
+__global__ __launch_bounds__(kPartThreads)
+__attribute__((amdgpu_waves_per_eu(4))) void rowpart_kernel(RowPartArgs a) {
+  __shared__ __align__(16) uint64_t ck[kPartCap + 8];
+  __shared__ __align__(16) float gz[kPartThreads / 4];
+  __shared__ float wmax[kPartThreads / kWave];
+  __shared__ double wsum[kPartThreads / kWave];
+  __shared__ int s_count;
+  __shared__ float s_tz;
+  __shared__ int s_tv;
+  const int row = blockIdx.x, part = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n4 = a.V / 4;
+  const int b4 = part * a.chunk4;
+  const int e4 = min(b4 + a.chunk4, n4);  // > b4: pieces are never empty
+  const float4* L4 =
+      reinterpret_cast<const float4*>(a.L + (int64_t)row * a.V);
+
+  // the piece, loaded once: unconditional loads (the tail repeats the last
+  // in-range vector) so that every load is in flight before the first use
+  float4 x[kPartVec];
+#pragma unroll
+  for (int i = 0; i < kPartVec; ++i)
+    x[i] = L4[min(b4 + tid + i * kPartThreads, e4 - 1)];
+  // vectors i < nv of this thread are inside the piece; the rest become -inf
+  const int nv = (e4 - b4 - tid + kPartThreads - 1) / kPartThreads;
+#pragma unroll
+  for (int i = 0; i < kPartVec; ++i) {
+    const bool in = i < nv;
+    x[i].x = in ? x[i].x : neg_inf();
+    x[i].y = in ? x[i].y : neg_inf();
+    x[i].z = in ? x[i].z : neg_inf();
+    x[i].w = in ? x[i].w : neg_inf();
+  }
+
+  // thread maximum; the maxima of groups of 4 threads go to LDS
+  float m = neg_inf();
+#pragma unroll
+  for (int i = 0; i < kPartVec; ++i)
+    m = fmaxf(fmaxf(m, fmaxf(x[i].x, x[i].y)), fmaxf(x[i].z, x[i].w));
+  float qm = fmaxf(m, Bits32<float>::from(dpp_i<kDppXor1>(Bits32<float>::to(m))));
+  qm = fmaxf(qm, Bits32<float>::from(dpp_i<kDppXor2>(Bits32<float>::to(qm))));
+  const float wm = wave_max(qm);
+  if (lane == 0) wmax[wave] = wm;
+  if ((lane & 3) == 0) gz[tid >> 2] = qm;
+  if (tid == 0) {
+    s_count = 0;
+    s_tz = neg_inf();
+  }
+  __syncthreads();
+  float M = wmax[0];
+#pragma unroll
+  for (int w = 1; w < kPartThreads / kWave; ++w) M = fmaxf(M, wmax[w]);
+  const float M2 = M * kLog2e;
+
+  // sum of 2^(z log2e - M2); padding (-inf) adds 0
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < kPartVec; ++i) {
+    const float e[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      sum += __builtin_amdgcn_exp2f(fmaf(e[c], kLog2e, -M2));
+  }
+  const double wsd = wave_sum((double)sum);
+  if (lane == 0) wsum[wave] = wsd;
+
+  // Selection bound: the K-th largest group maximum (with multiplicity).
+  // K groups hold an element >= it, so every element of the piece's best K
+  // is >= it.  Thread t counts, for group t/4, the group maxima above and
+  // at-or-above it in a quarter of the table; a group whose value has fewer
+  // than K maxima above and at least K at-or-above is the K-th.
+  {
+    constexpr int NG = kPartThreads / 4, QG = NG / 4;
+    const float z = gz[tid >> 2];
+    const float4* g4 = reinterpret_cast<const float4*>(gz + (tid & 3) * QG);
+    int gt = 0, ge = 0;
+#pragma unroll
+    for (int j = 0; j < QG / 4; ++j) {
+      const float4 g = g4[j];
+      gt += (g.x > z) + (g.y > z) + (g.z > z) + (g.w > z);
+      ge += (g.x >= z) + (g.y >= z) + (g.z >= z) + (g.w >= z);
+    }
+    gt += dpp_i<kDppXor1>(gt);
+    gt += dpp_i<kDppXor2>(gt);
+    ge += dpp_i<kDppXor1>(ge);
+    ge += dpp_i<kDppXor2>(ge);
+    if ((tid & 3) == 0 && gt <= a.K - 1 && ge >= a.K) s_tz = z;  // one value
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double tot = 0.0;
+#pragma unroll
+    for (int w = 0; w < kPartThreads / kWave; ++w) tot += wsum[w];
+    a.pm[(int64_t)row * a.parts + part] = M2;
+    a.ps[(int64_t)row * a.parts + part] = tot;
+  }
+  float tz = s_tz;
+  int tv = 0x7fffffff;
+  // -inf: fewer than K groups hold data (a tiny piece); take everything
+  bool all = tz == neg_inf();
+
+  // ballot-compacted append of the lanes with `take` to the LDS buffer
+  auto offer = [&](float z, int v, bool take) __attribute__((always_inline)) {
+    const uint64_t bal = __ballot(take);
+    if (bal == 0) return;
+    int base = 0;
+    if (lane == 0) base = atomicAdd(&s_count, __popcll(bal));
+    base = __builtin_amdgcn_readfirstlane(base);
+    if (take) {
+      const int pos =
+          base + __builtin_amdgcn_mbcnt_hi(
+                     (uint32_t)(bal >> 32),
+                     __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+      if (pos < kPartCap) ck[pos] = zv_key(z, v);
+    }
+  };
+  // common case: collect every element >= the bound from registers (the
+  // bound is finite here, so the -inf padding never qualifies)
+  if (!all) {
+    // a fresh copy of the token base keeps the compiler from computing the
+    // token numbers early and holding them across the phases above
+    int vc = 4 * (b4 + tid);
+    asm volatile("" : "+v"(vc));
+#pragma unroll
+    for (int i = 0; i < kPartVec; ++i) {
+      const int v0 = vc + 4 * kPartThreads * i;
+      const float e[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) offer(e[c], v0 + c, e[c] >= tz);
+    }
+  }
+  __syncthreads();
+  int count = s_count;
+  if (all || count > kPartCap) {
+    // rare: a tiny piece (take everything) or an overflowing buffer.  The
+    // piece is read again from memory, with the bound tightened on each
+    // overflow to the K-th best (logit desc, token asc) of the kept
+    // elements: at least kPartCap - K of them drop out per round.
+    for (;;) {
+      if (count > kPartCap) {
+        for (int e = tid; e < kPartCap; e += kPartThreads) {
+          const uint64_t key = ck[e];
+          int rank = 0;
+          for (int j = 0; j < kPartCap; ++j) rank += ck[j] > key;
+          if (rank == a.K - 1) {
+            s_tz = ordered_to_float((uint32_t)(key >> 32));
+            s_tv = 0x7fffffff - (int)(uint32_t)key;
+          }
+        }
+        __syncthreads();
+        tz = s_tz;
+        tv = s_tv;
+        all = false;
+      }
+      __syncthreads();
+      if (tid == 0) s_count = 0;
+      __syncthreads();
+      // a uniform trip count per wave keeps every lane in the ballots
+      for (int j0 = b4 + wave * kWave; j0 < e4; j0 += kPartThreads) {
+        const int j4 = j0 + lane;
+        const bool ok = j4 < e4;
+        const float4 y = L4[ok ? j4 : e4 - 1];
+        const float e[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int v = 4 * j4 + c;
+          offer(e[c], v,
+                ok && (all || e[c] > tz || (e[c] == tz && v <= tv)));
+        }
+      }
+      __syncthreads();
+      count = s_count;
+      if (count <= kPartCap) break;
+    }
+  }
+
+  // rank the kept elements (keys are distinct); the first K form the
+  // piece's sorted list.  Keys are compared eight at a time from 16-byte
+  // LDS reads; the buffer is padded with zero keys, below every real key.
+  if (tid < 8) ck[count + tid] = 0;
+  __syncthreads();
+  const int64_t ob = ((int64_t)row * a.parts + part) * a.K;
+  const int nblk = (count + 7) / 8;
+  for (int e = tid; e < count; e += kPartThreads) {
+    const uint64_t key = ck[e];
+    int rank = 0;
+    const ulonglong2* c2 = reinterpret_cast<const ulonglong2*>(ck);
+    for (int j = 0; j < nblk; ++j) {
+      const ulonglong2 k0 = c2[4 * j], k1 = c2[4 * j + 1];
+      const ulonglong2 k2 = c2[4 * j + 2], k3 = c2[4 * j + 3];
+      rank += (k0.x > key) + (k0.y > key) + (k1.x > key) + (k1.y > key) +
+              (k2.x > key) + (k2.y > key) + (k3.x > key) + (k3.y > key);
+    }
+    if (rank < a.K) {
+      a.cz[ob + rank] = ordered_to_float((uint32_t)(key >> 32));
+      a.cv[ob + rank] = 0x7fffffff - (int)(uint32_t)key;
+    }
+  }
+  for (int r = count + tid; r < a.K; r += kPartThreads) {
+    a.cz[ob + r] = neg_inf();
+    a.cv[ob + r] = 0x7fffffff;
+  }
+}
+
+__global__ __launch_bounds__(256) void rowmerge_kernel(RowMergeArgs a) {
+  __shared__ float mz[kPartMaxParts * kPartMaxK];
+  __shared__ int mv[kPartMaxParts * kPartMaxK];
+  __shared__ float s_pm[kPartMaxParts];
+  __shared__ double s_ps[kPartMaxParts];
+  __shared__ float s_lse;
+  __shared__ int s_valid;
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int n = a.parts * a.K;
+  const int64_t ib = (int64_t)row * n;
+  if (tid == 0) s_valid = 0;
+  if (tid < a.parts) {
+    s_pm[tid] = a.pm[(int64_t)row * a.parts + tid];
+    s_ps[tid] = a.ps[(int64_t)row * a.parts + tid];
+  }
+  int nvalid = 0;
+  for (int e = tid; e < n; e += 256) {
+    mz[e] = a.cz[ib + e];
+    mv[e] = a.cv[ib + e];
+    nvalid += mv[e] != 0x7fffffff;
+  }
+  __syncthreads();
+  nvalid = wave_sum(nvalid);
+  if ((tid & 63) == 0 && nvalid) atomicAdd(&s_valid, nvalid);
+  if (tid == 0) {
+    float M = neg_inf();
+    for (int p = 0; p < a.parts; ++p) M = fmaxf(M, s_pm[p]);
+    double tot = 0.0;
+    for (int p = 0; p < a.parts; ++p)
+      if (s_pm[p] != neg_inf()) tot += s_ps[p] * exp2((double)s_pm[p] - M);
+    s_lse = (float)(kLn2 * ((double)M + log2(tot)));
+  }
+  __syncthreads();
+  const float lse = s_lse;
+  const int64_t ob = (int64_t)row * a.kstride;
+  for (int e = tid; e < n; e += 256) {
+    const float z = mz[e];
+    const int v = mv[e];
+    if (v == 0x7fffffff) continue;
+    const int p = e / a.K;
+    int rank = e - p * a.K;
+    for (int q = 0; q < a.parts; ++q) {
+      if (q == p) continue;
+      // entries of list q before (z, v); lists are sorted, padding last
+      const float* qz = mz + q * a.K;
+      const int* qv = mv + q * a.K;
+      int lo = 0, hi = a.K;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (zv_before(qz[mid], qv[mid], z, v))
+          lo = mid + 1;
+        else
+          hi = mid;
+      }
+      rank += lo;
+    }
+    if (rank < a.K) {
+      a.ltok[ob + rank] = v;
+      a.llp[ob + rank] = z - lse;  // log pi
+    }
+  }
+  for (int r = min(s_valid, a.K) + tid; r < a.K; r += 256) {
+    a.ltok[ob + r] = -1;
+    a.llp[ob + r] = neg_inf();
+  }
+  if (tid == 0) a.lse[row] = lse;
+}
+
+// ---------------------------------------------------------------------
 
 struct BestFirstArgs {
   int B, V, n_max;
@@ -397,6 +706,36 @@ hipError_t launch_rowsel(const float* L, int rows, int V, int B, int K,
                          hipStream_t s) {
   RowSelArgs a{L, V, B, K, kstride, only_flagged, vec_ok, lse, ltok, llp};
   hipLaunchKernelGGL(rowsel_kernel, dim3(rows), dim3(kRowThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+int rowpart_pieces(int V) {
+  const int n4 = V / 4;
+  const int per = kPartThreads * kPartVec;
+  return n4 <= 0 ? 0 : (n4 + per - 1) / per;
+}
+
+bool rowpart_ok(int V, int K, int vec_ok) {
+  if (!vec_ok || V % 4 != 0 || K < 1 || K > kPartMaxK) return false;
+  const int parts = rowpart_pieces(V);
+  if (parts < 1 || parts > kPartMaxParts) return false;
+  const int n4 = V / 4, chunk4 = (n4 + parts - 1) / parts;
+  return (parts - 1) * chunk4 < n4 && chunk4 <= kPartThreads * kPartVec;
+}
+
+hipError_t launch_rowpart(const float* L, int rows, int V, int K, int kstride,
+                          float* pm, double* ps, float* cz, int32_t* cv,
+                          float* lse, int32_t* ltok, float* llp,
+                          hipStream_t s) {
+  const int parts = rowpart_pieces(V);
+  const int n4 = V / 4;
+  RowPartArgs a{L, V, K, parts, (n4 + parts - 1) / parts, pm, ps, cz, cv};
+  hipLaunchKernelGGL(rowpart_kernel, dim3(rows, parts), dim3(kPartThreads),
+                     0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  RowMergeArgs m{K, parts, kstride, pm, ps, cz, cv, lse, ltok, llp};
+  hipLaunchKernelGGL(rowmerge_kernel, dim3(rows), dim3(256), 0, s, m);
   return hipGetLastError();
 }
 

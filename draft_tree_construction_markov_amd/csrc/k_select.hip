@@ -19,54 +19,78 @@ namespace pct {
 // |dM| <= 2 r 2^-24 sum|u w| (each side's recursive-sum bound; doubled
 // again for safety) plus a few ulps of |z| for the final fp32 adds.
 
-// Per L row, the kSeedT tokens of largest L: each thread keeps its best
-// element, then the workgroup keeps the kSeedT best of those (any subset is
-// a valid seed; this one is nearly the row's top kSeedT).
+// Per L row, kSeedT tokens of large L.  The row is cut into kRowTopPieces
+// pieces with one workgroup each (enough workgroups to keep every CU
+// streaming); each thread keeps its best element of the piece and the piece
+// contributes the kSeedT / kRowTopPieces best of those.  Any subset is a
+// valid seed; this one is close to the row's top kSeedT.
+constexpr int kRowTopPieces = 4;
+constexpr int kRowTopSlots = kSeedT / kRowTopPieces;
+
 __global__ __launch_bounds__(256) void row_top_kernel(const float* L, int V,
                                                        int64_t lstride,
                                                        int vec_ok,
                                                        int32_t* rowtop) {
-  __shared__ float sz[256];
-  __shared__ int32_t sv[256];
-  const int row = blockIdx.x, tid = threadIdx.x;
+  __shared__ __align__(16) float sz[256];
+  __shared__ __align__(16) int32_t sv[256];
+  const int row = blockIdx.x, piece = blockIdx.y, tid = threadIdx.x;
   const float* Lr = L + (int64_t)row * lstride;
+  // piece bounds in tokens, a multiple of 4 apart so that vectors align
+  const int span = ((V + 4 * kRowTopPieces - 1) / (4 * kRowTopPieces)) * 4;
+  const int v0 = min(piece * span, V), v1 = min(v0 + span, V);
   float bz = neg_inf();
   int32_t bv = 0x7fffffff;
+  // Within a thread the tokens only grow, so a strict comparison keeps the
+  // smallest token among equal logits: a max and a select per element.
+  auto see = [&](float z, int v) __attribute__((always_inline)) {
+    const bool b = z > bz;
+    bz = b ? z : bz;
+    bv = b ? v : bv;
+  };
   if (vec_ok) {
     const float4* L4 = reinterpret_cast<const float4*>(Lr);
-    const int n4 = V / 4;
-    // four independent 16-byte loads in flight per thread
-    for (int i0 = tid; i0 < n4; i0 += 4 * 256) {
-      float4 x[4];
+    const int i0b = v0 / 4, i1 = v1 / 4;  // whole vectors; V % 4 == 0 here
+    // eight independent 16-byte loads in flight per thread; out-of-range
+    // slots reload the first vector of the piece and are masked to -inf
+    for (int i0 = i0b + tid; i0 < i1; i0 += 8 * 256) {
+      float4 x[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const int i = i0 + u * 256;
-        x[u] = i < n4 ? L4[i] : make_float4(neg_inf(), neg_inf(), neg_inf(),
-                                            neg_inf());
+        x[u] = L4[i < i1 ? i : i0b];
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int v = 4 * (i0 + u * 256);
-        if (zv_before(x[u].x, v, bz, bv)) { bz = x[u].x; bv = v; }
-        if (zv_before(x[u].y, v + 1, bz, bv)) { bz = x[u].y; bv = v + 1; }
-        if (zv_before(x[u].z, v + 2, bz, bv)) { bz = x[u].z; bv = v + 2; }
-        if (zv_before(x[u].w, v + 3, bz, bv)) { bz = x[u].w; bv = v + 3; }
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * 256;
+        const bool in = i < i1;
+        const int v = 4 * i;
+        see(in ? x[u].x : neg_inf(), v);
+        see(in ? x[u].y : neg_inf(), v + 1);
+        see(in ? x[u].z : neg_inf(), v + 2);
+        see(in ? x[u].w : neg_inf(), v + 3);
       }
     }
-    for (int v = 4 * n4 + tid; v < V; v += 256)
-      if (zv_before(Lr[v], v, bz, bv)) { bz = Lr[v]; bv = v; }
   } else {
-    for (int v = tid; v < V; v += 256)
-      if (zv_before(Lr[v], v, bz, bv)) { bz = Lr[v]; bv = v; }
+    for (int v = v0 + tid; v < v1; v += 256) see(Lr[v], v);
   }
   sz[tid] = bz;
   sv[tid] = bv;
-  // slots without a distinct token (V < kSeedT) stay -1 and are skipped
-  if (tid < kSeedT) rowtop[(int64_t)row * kSeedT + tid] = -1;
+  // slots without a distinct token (tiny pieces) stay -1 and are skipped
+  int32_t* out = rowtop + (int64_t)row * kSeedT + piece * kRowTopSlots;
+  if (tid < kRowTopSlots) out[tid] = -1;
   __syncthreads();
+  // rank of the thread's best among the 256 (16-byte LDS reads, unrolled)
   int rank = 0;
-  for (int j = 0; j < 256; ++j) rank += zv_before(sz[j], sv[j], bz, bv);
-  if (rank < kSeedT && bv < V) rowtop[(int64_t)row * kSeedT + rank] = bv;
+  const float4* z4 = reinterpret_cast<const float4*>(sz);
+  const int4* v4 = reinterpret_cast<const int4*>(sv);
+#pragma unroll 8
+  for (int j = 0; j < 64; ++j) {
+    const float4 z = z4[j];
+    const int4 v = v4[j];
+    rank += zv_before(z.x, v.x, bz, bv) + zv_before(z.y, v.y, bz, bv) +
+            zv_before(z.z, v.z, bz, bv) + zv_before(z.w, v.w, bz, bv);
+  }
+  if (rank < kRowTopSlots && bv < V) out[rank] = bv;
 }
 
 __device__ __forceinline__ float dot_bf16(const uint16_t* u, const uint16_t* w,
@@ -759,8 +783,8 @@ __global__ __launch_bounds__(256) void finalize_kernel(
 
 hipError_t launch_rowtop(const float* L, int rows, int V, int64_t lstride,
                          int vec_ok, int32_t* rowtop, hipStream_t s) {
-  hipLaunchKernelGGL(row_top_kernel, dim3(rows), dim3(256), 0, s, L, V,
-                     lstride, vec_ok, rowtop);
+  hipLaunchKernelGGL(row_top_kernel, dim3(rows, kRowTopPieces), dim3(256), 0,
+                     s, L, V, lstride, vec_ok, rowtop);
   return hipGetLastError();
 }
 

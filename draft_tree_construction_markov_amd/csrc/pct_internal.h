@@ -171,6 +171,16 @@ hipError_t launch_bestfirst(int batch, int B, int V, int n_max, int klist,
                             int32_t* flag, int slow, hipStream_t s);
 constexpr int kAdaptiveShortList = 64;  // list length of the first pass
 constexpr int kAdaptiveMaxNodes = 1024;
+// single-read row statistics: lists up to kPartMaxK, rows cut into at most
+// kPartMaxParts register-resident pieces
+constexpr int kPartMaxK = 128;
+constexpr int kPartMaxParts = 8;
+int rowpart_pieces(int V);
+bool rowpart_ok(int V, int K, int vec_ok);
+hipError_t launch_rowpart(const float* L, int rows, int V, int K, int kstride,
+                          float* pm, double* ps, float* cz, int32_t* cv,
+                          float* lse, int32_t* ltok, float* llp,
+                          hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
 hipError_t launch_mask(int batch, int N, const int32_t* parent,
                        const int32_t* n_nodes, uint64_t* mask, hipStream_t s);

@@ -79,6 +79,23 @@ def test_exhausted_tree_and_small_vocab():
     assert all(int(x) == 5 + 25 + 125 for x in g["n_star"])
 
 
+def test_row_lists_bound_overflow():
+    # The single-read row statistics cut a row of V = 151936 into 4 pieces
+    # of 9496 16-byte vectors, vector j of a piece going to thread j % 512.
+    # Large logits only on threads 0..251 (63 groups of 4, fewer than the 64
+    # list entries) make the first selection bound loose: over 2048
+    # candidates pass it, so the bound is tightened and the piece re-read.
+    V = 151936
+    rng = np.random.default_rng(7)
+    L = rng.normal(size=(2, 3, V)).astype(np.float32)
+    vec = np.arange(V) // 4
+    slot = (vec - (vec // 9496) * 9496) % 512
+    L[:, :, slot < 252] += 10.0
+    ctx = np.array([700, 9000], np.int32)
+    g, bins = run_compare(L, ctx, 64, None, "bound-overflow")
+    assert all(int(x) == 64 for x in g["n_star"])
+
+
 def test_uniform_rows_ties():
     L = np.zeros((2, 4, 700), np.float32)
     ctx = np.array([512, 30000], np.int32)
