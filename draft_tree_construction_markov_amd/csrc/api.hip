@@ -116,6 +116,7 @@ struct TreeWs {
   float* gz;
   int32_t* gv;
   uint64_t* pool_key;
+  uint4* upack;  // packed U rows of one depth's parents (MFMA plans only)
 };
 
 size_t carve_tree(const pct_tree_shape* sh, const TreePlan& tp, void* ws,
@@ -136,6 +137,11 @@ size_t carve_tree(const pct_tree_shape* sh, const TreePlan& tp, void* ws,
   w.gz = c.take<float>(tp.max_cap_P);
   w.gv = c.take<int32_t>(tp.max_cap_P);
   w.pool_key = c.take<uint64_t>((size_t)sh->batch * tp.pool_n);
+  // packed U rows: whole 32-parent blocks of r/8 16-byte chunks
+  const bool mfma = tp.k1[1].kind == K1_MFMA;
+  w.upack = c.take<uint4>(mfma ? (size_t)((tp.max_P + 31) / 32 * 32) *
+                                     (sh->r / 8)
+                               : 0);
   return c.off;
 }
 
@@ -325,6 +331,9 @@ pct_status pct_build_tree(const pct_tree_shape* shape, const float* L,
   sa.V = V;
   sa.k = sh.k;
   sa.use_seed = sh.k <= kSeedT;
+  // every depth of an MFMA plan reads its parents' U rows packed; init and
+  // expand write them for the depth that follows
+  sa.upack = tp.k1[1].kind == K1_MFMA ? w.upack : nullptr;
 
   Frontier f0{w.ftok[0], w.fpid[0], w.flrow[0], w.fs[0], w.ftheta[0]};
   Frontier f1{w.ftok[1], w.fpid[1], w.flrow[1], w.fs[1], w.ftheta[1]};
@@ -381,6 +390,7 @@ pct_status pct_build_tree(const pct_tree_shape* shape, const float* L,
     a.gv = w.gv;
     a.cap = pl.cap;
     a.z_out = nullptr;
+    a.upack = sa.upack;
     {
       ProfScope ps(PROF_MARKOV, P, s);
       e = launch_k1(pl, a, s);

@@ -148,13 +148,26 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
     row = row < 0 ? 0 : (row >= a.L_rows ? a.L_rows - 1 : row);
     lrow[b] = (!STAGED && has_L) ? a.L + row * a.lstride : nullptr;
     lslot[b] = STAGED ? pc / a.group_fp - g0 : 0;
-    const uint4* up =
-        reinterpret_cast<const uint4*>(a.U) + (int64_t)tok * CH + h;
+    if (a.upack != nullptr) {
+      // packed rows: one contiguous 1 KB load per rank step; a block past
+      // the parents is not read
+      const uint4* up = a.upack + (int64_t)((pw + 32 * b) >> 5) * R16 * 64 + lane;
+      const bool blk = pw + 32 * b < a.P;
 #pragma unroll
-    for (int kk = 0; kk < R16; ++kk) {
-      uint4 raw = up[2 * kk];
-      if (!valid) raw = make_uint4(0, 0, 0, 0);
-      uf[b][kk] = __builtin_bit_cast(bf16x8, raw);
+      for (int kk = 0; kk < R16; ++kk) {
+        uint4 raw = blk ? up[kk * 64] : make_uint4(0, 0, 0, 0);
+        if (!valid) raw = make_uint4(0, 0, 0, 0);
+        uf[b][kk] = __builtin_bit_cast(bf16x8, raw);
+      }
+    } else {
+      const uint4* up =
+          reinterpret_cast<const uint4*>(a.U) + (int64_t)tok * CH + h;
+#pragma unroll
+      for (int kk = 0; kk < R16; ++kk) {
+        uint4 raw = up[2 * kk];
+        if (!valid) raw = make_uint4(0, 0, 0, 0);
+        uf[b][kk] = __builtin_bit_cast(bf16x8, raw);
+      }
     }
     thr[b] = valid ? (a.theta ? a.theta[p] : neg_inf()) : pos_inf();
     cm2[b] = neg_inf();

@@ -421,6 +421,14 @@ __global__ __launch_bounds__(64) void init_kernel(int B, const int32_t* anchor,
   } else {
     th = seed_theta(sa, a, q * B, lane);
   }
+  if (sa.upack != nullptr) {
+    // packed U row of this parent (parent q of the depth-1 frontier)
+    const int ch = sa.r / 8;
+    const uint4* urow = reinterpret_cast<const uint4*>(sa.U) +
+                        (int64_t)min(max(a, 0), sa.V - 1) * ch;
+    for (int c = lane; c < ch; c += 64)
+      sa.upack[upack_index(q, c, ch / 2)] = urow[c];
+  }
   if (lane == 0) {
     f.tok[q] = a;
     f.pid[q] = -1;
@@ -696,6 +704,20 @@ __global__ __launch_bounds__(kExpandWaves * 64) void expand_kernel(
       th = seed_theta(a.seed, ctok[bcand[i]], row, lane);
     }
     if (lane == 0) a.nxt.theta[q * a.Fn + i] = th;
+  }
+  // packed U rows of the next depth's parents (the fused kernel's operand
+  // order), from the prefetched rows when there are any
+  if (a.seed.upack != nullptr) {
+    const uint4* Ug = reinterpret_cast<const uint4*>(a.seed.U);
+    const int cr = a.seed.r / 8;
+    for (int i = tid; i < a.Fn * cr; i += NT) {
+      const int j = i / cr, c = i % cr;
+      const int cb = bcand[j];
+      const uint4 v =
+          upref ? upre[cb * cr + c]
+                : Ug[(int64_t)min(max(ctok[cb], 0), a.seed.V - 1) * cr + c];
+      a.seed.upack[upack_index(q * a.Fn + j, c, cr / 2)] = v;
+    }
   }
 }
 

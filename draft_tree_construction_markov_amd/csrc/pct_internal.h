@@ -42,6 +42,10 @@ struct K1Args {
   int32_t* gv;     // [P][cap]
   int cap;
   float* z_out;    // [P][V] optional
+  // U rows of the parents in MFMA operand order (null: gathered from U):
+  // 16-byte chunk c of parent p's row at ((p/32) * r/16 + c/2) * 64 +
+  // (c%2) * 32 + p%32
+  const uint4* upack;
 };
 
 enum K1Kind { K1_MFMA = 0, K1_SIMPLE = 1 };
@@ -121,7 +125,15 @@ struct SeedArgs {
   const void* W;
   int uw_bf16, r, V, k;
   int use_seed;
+  uint4* upack;  // packed U rows of the next parents (null: not written)
 };
+
+// Index of 16-byte chunk c (of 2*R16 per row) of parent p in the packed U
+// layout read by the fused kernel: one 64-lane MFMA operand load per
+// (32-parent block, rank step) covers 1 KB of consecutive memory.
+__host__ __device__ inline int64_t upack_index(int p, int c, int R16) {
+  return ((int64_t)(p >> 5) * R16 + (c >> 1)) * 64 + (c & 1) * 32 + (p & 31);
+}
 
 struct ExpandArgs {
   int d, B, Fp, Fn, k, N, batch;
