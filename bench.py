@@ -19,7 +19,8 @@ Prints one JSON line (rank 0):
                kernel changed since the counters were taken
   cpu_baseline the CPU oracle on a bounded sample of the same workload
   adaptive     the adaptive best-first build (batch 64, n_max 1024) with its
-               row-statistics kernel against HBM peak
+               row-statistics kernels (single-read pieces, their merge and
+               the full-length pass) against HBM peak
 """
 from __future__ import annotations
 
@@ -287,7 +288,9 @@ def bench_adaptive(args, pct, synth, torch, dev):
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4),
                          "traffic": traffic_of("rowsel"),  # per step
-                         "kernel": "rowsel_kernel (1024 rows/step)",
+                         "kernel": "row statistics: rowpart_kernel + "
+                                   "rowmerge_kernel + full-length "
+                                   "rowsel_kernel pass (1024 rows/step)",
                          "ms_per_step": round(rs_step, 5),
                          "launches_per_step": rs_n // args.steps},
             "bestfirst_ms_per_step": round(bf_ms / args.steps, 5)}
