@@ -9,6 +9,9 @@
 
 namespace pct {
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+
 // ---------------------------------------------------------------------
 // Seeds.  For a parent p, theta_p = (k-th largest z over a small token
 // subset) - margin is a lower bound of the k-th largest z over the whole
@@ -267,15 +270,18 @@ __device__ void wave_topk(const float* gz, const int32_t* gv, int cnt, int k,
 // candidates take k passes of wave-wide arg-max.
 template <typename F>
 __device__ void wave_topk_rank(const float* gz, const int32_t* gv, int cnt,
-                               int k, int lane, float2* scratch, F&& emit) {
+                               int k, int lane, float2* scratch, F&& emit,
+                               bool have = false, float hz = 0.f,
+                               int32_t hv = 0) {
   if (cnt > kWave) {
     wave_topk(gz, gv, cnt, k, lane, [&](int i, float z, int32_t v) {
       if (lane == 0) emit(i, z, v);
     });
     return;
   }
-  const float cz = lane < cnt ? gz[lane] : neg_inf();
-  const int32_t cv = lane < cnt ? gv[lane] : 0x7fffffff;
+  // (hz, hv): this lane's slot, already loaded by the caller when `have`
+  const float cz = lane < cnt ? (have ? hz : gz[lane]) : neg_inf();
+  const int32_t cv = lane < cnt ? (have ? hv : gv[lane]) : 0x7fffffff;
   scratch[lane] = make_float2(cz, __int_as_float(cv));
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -452,7 +458,10 @@ __device__ float seed_theta_lds(const SeedArgs& sa, const uint4* wrows,
   const int t = lane & 31, h = lane >> 5;
   const int half = sa.r / 16;  // chunks per half of the rank dimension
   const int cs = sa.r / 8 + 1;  // W row stride in chunks (one pad chunk)
-  // four independent partial sums keep the dependent chains short
+  // four independent partial sums keep the dependent chains short; each
+  // step is a two-product bf16 dot (at most one fp32 rounding per two exact
+  // products, inside the margin below), on the values and on their
+  // magnitudes (sign bits cleared)
   float acc[4] = {0.f, 0.f, 0.f, 0.f}, aa[4] = {0.f, 0.f, 0.f, 0.f};
   for (int c = h * half; c < (h + 1) * half; ++c) {
     const uint4 a4 = urow[c], b4 = wrows[t * cs + c];
@@ -460,14 +469,12 @@ __device__ float seed_theta_lds(const SeedArgs& sa, const uint4* wrows,
     const uint32_t wb[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float u0 = __uint_as_float(ua[i] << 16);
-      const float u1 = __uint_as_float(ua[i] & 0xffff0000u);
-      const float w0 = __uint_as_float(wb[i] << 16);
-      const float w1 = __uint_as_float(wb[i] & 0xffff0000u);
-      acc[i] = fmaf(u0, w0, acc[i]);
-      aa[i] += fabsf(u0 * w0);
-      acc[i] = fmaf(u1, w1, acc[i]);
-      aa[i] += fabsf(u1 * w1);
+      acc[i] = __builtin_amdgcn_fdot2_f32_bf16(
+          __builtin_bit_cast(bf16x2, ua[i]), __builtin_bit_cast(bf16x2, wb[i]),
+          acc[i], false);
+      aa[i] = __builtin_amdgcn_fdot2_f32_bf16(
+          __builtin_bit_cast(bf16x2, ua[i] & 0x7fff7fffu),
+          __builtin_bit_cast(bf16x2, wb[i] & 0x7fff7fffu), aa[i], false);
     }
   }
   const float m4 = (acc[0] + acc[1]) + (acc[2] + acc[3]);
@@ -580,6 +587,17 @@ __global__ __launch_bounds__(kExpandWaves * 64) void expand_kernel(
     }
   };
   if (staged) load_group(0);
+  // the first 64 candidate slots of this wave's first parent, loaded now so
+  // that they arrive while the partials and the seed operands are staged
+  // (slots past the parent's count are never used)
+  float hz = neg_inf();
+  int32_t hv = 0x7fffffff;
+  if (wave < a.Fp && lane < a.cap) {
+    const int64_t o =
+        (int64_t)(a.shared_stats ? q : q * a.Fp + wave) * a.cap + lane;
+    hz = a.gz[o];
+    hv = a.gv[o];
+  }
   if (lseed)
     stage_seed_rows(a.seed, row, wrows, lval, vt, tid, NT);
   for (int i = tid; i < NC; i += NT) crank[i] = 0;
@@ -627,7 +645,7 @@ __global__ __launch_bounds__(kExpandWaves * 64) void expand_kernel(
                        cpid[c] = pid;
                        ctok[c] = v;
                        a.pool_key[(int64_t)q * a.pool_n + pid] = key;
-                     });
+                     }, g0 == 0, hz, hv);
     }
   }
   __syncthreads();
