@@ -561,6 +561,9 @@ __global__ __launch_bounds__(kExpandWaves * 64) void expand_kernel(
   const int ch = a.seed.r / 8;
   const bool staged = !a.shared_stats && a.n_slices <= kStageSlices;
   const bool upref = lseed && NC <= kUPre;
+  // each wave prefetches its parent's children when they fill whole
+  // 64-chunk instructions
+  const bool upwave = upref && (a.k * ch) % 64 == 0;
   // partials of a group of up to 16 parents into LDS; the first group's
   // loads are issued before the seed staging so that the two overlap
   constexpr int kStageIt = kExpandWaves * kStageSlices / NT;
@@ -646,12 +649,32 @@ __global__ __launch_bounds__(kExpandWaves * 64) void expand_kernel(
                        ctok[c] = v;
                        a.pool_key[(int64_t)q * a.pool_n + pid] = key;
                      }, g0 == 0, hz, hv);
+      if (upwave) {
+        // this parent's children's U rows, issued as soon as their tokens
+        // are known (direct global->LDS loads, 64 chunks per instruction)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const uint4* Ug = reinterpret_cast<const uint4*>(a.seed.U);
+        const int base = j * a.k * ch;
+        for (int i0 = 0; i0 < a.k * ch; i0 += 64) {
+          const int i = i0 + lane;
+          const int c = j * a.k + i / ch, cc = i % ch;
+          const int tok = min(max(ctok[c], 0), a.seed.V - 1);
+          __builtin_amdgcn_global_load_lds(
+              (const __attribute__((address_space(1))) void*)(
+                  Ug + (int64_t)tok * ch + cc),
+              (__attribute__((address_space(3))) void*)(upre + base + i0), 16,
+              0, 0);
+        }
+      }
     }
   }
   __syncthreads();
 
-  // U rows of every child, in flight while the beam is ranked
-  if (upref) {
+  // U rows of every child, in flight while the beam is ranked (when the
+  // waves did not issue their own children's rows above)
+  if (upref && !upwave) {
     const uint4* Ug = reinterpret_cast<const uint4*>(a.seed.U);
     for (int i0 = wave * 64; i0 < NC * ch; i0 += NT) {
       const int i = min(i0 + lane, NC * ch - 1);
