@@ -103,8 +103,9 @@ def test_markov_tree_parity(batch, B, V, k, beam, N, r):
 
 
 @pytest.mark.parametrize("batch,B,V,k,beam,N,r,reqs", [
-    # frontiers above 256 parents take the ping-pong kernel: two parent
-    # tiles, one 32-row sub-tile per slice (tail steps), ragged last tile
+    # frontiers above 256 parents take the 8-wave fused kernel (512
+    # parents per workgroup): 576-640 parents make two parent tiles, the
+    # second partly empty; ragged last vocabulary tile
     (40, 3, 3000, 8, 16, 64, 256, None),
     (36, 4, 5000, 8, 16, 96, 128, None),          # rank 128
     (33, 3, 2002, 8, 16, 64, 256, None),          # V % 4 != 0: other kernel
