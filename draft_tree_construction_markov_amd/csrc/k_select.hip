@@ -779,6 +779,10 @@ __global__ __launch_bounds__(1024) void topn_kernel(TopNArgs a) {
     inv[i] = -1;
   }
   __syncthreads();
+  // A stage with stride <= 32 pairs elements inside one 128-element block
+  // per wave (pair i of the wave's 64 touches 128*(i/64) .. +127), so the
+  // waves need no workgroup barrier between two such stages, only a wave
+  // fence; a stage with a larger stride is fenced by workgroup barriers.
   for (int size = 2; size <= n2; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       for (int i = tid; i < n2 / 2; i += 1024) {
@@ -794,7 +798,14 @@ __global__ __launch_bounds__(1024) void topn_kernel(TopNArgs a) {
           id[hi] = t;
         }
       }
-      __syncthreads();
+      const int next = stride > 1 ? stride >> 1 : (2 * size <= n2 ? size : 0);
+      if (stride > 32 || next > 32 || next == 0) {
+        __syncthreads();
+      } else {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
     }
   }
   const int n = min(a.N, a.pool_n);
