@@ -121,8 +121,10 @@ K1Plan plan_k1(int P, int V, int r, int k, int uw_dtype, bool has_uw,
       pl.NB = 1;
       pl.NW = 1;
     } else if (P <= 256) {
-      pl.NB = 2;
-      pl.NW = 4;
+      // 32 parents per wave, 8 waves: two waves share each SIMD (64 parents
+      // per wave would leave one)
+      pl.NB = 1;
+      pl.NW = 8;
     } else {
       pl.NB = 2;
       pl.NW = 8;
@@ -158,7 +160,7 @@ K1Plan plan_k1(int P, int V, int r, int k, int uw_dtype, bool has_uw,
       pl.lds = lists_of(pl.NW);
       pl.lds_total = wbytes + direct_l + pl.lds;
     }
-    if (pl.NB == 1 && pl.NW != 1) pl.NW = 1;
+    if (pl.NB == 1 && pl.NW != 1 && pl.NW != 8) pl.NW = 1;
     int per_cu = (int)(kLdsPerCU / pl.lds_total);
     if (per_cu < 1) per_cu = 1;
     const int by_waves = 8 / pl.NW > 0 ? 8 / pl.NW : 1;

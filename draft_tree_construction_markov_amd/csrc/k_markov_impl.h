@@ -386,7 +386,9 @@ hipError_t go_mfma(const K1Plan& pl, const K1Args& a, hipStream_t s) {
 template <int R16, bool STAGED>
 hipError_t launch_mfma_rank(const K1Plan& pl, const K1Args& a,
                             hipStream_t s) {
-  if (pl.NB == 1) return go_mfma<1, 1, R16, STAGED>(pl, a, s);
+  if (pl.NB == 1)
+    return pl.NW == 8 ? go_mfma<1, 8, R16, STAGED>(pl, a, s)
+                      : go_mfma<1, 1, R16, STAGED>(pl, a, s);
   switch (pl.NW) {
     case 8: return go_mfma<2, 8, R16, STAGED>(pl, a, s);
     case 4: return go_mfma<2, 4, R16, STAGED>(pl, a, s);
