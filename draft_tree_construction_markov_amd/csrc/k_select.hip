@@ -409,32 +409,34 @@ __device__ __forceinline__ bool seed_by_mfma(const SeedArgs& sa) {
 
 // ---------------------------------------------------------------------
 // Depth-1 frontier: the anchor of each request.
-__global__ __launch_bounds__(64) void init_kernel(int B, const int32_t* anchor,
-                                                  Frontier f, int32_t* gcnt,
-                                                  SeedArgs sa) {
+// Four waves stage the seed operands (their loads in flight together); the
+// first wave computes the threshold.
+constexpr int kInitThreads = 256;
+__global__ __launch_bounds__(kInitThreads) void init_kernel(
+    int B, const int32_t* anchor, Frontier f, int32_t* gcnt, SeedArgs sa) {
   __shared__ uint4 wrows[kSeedT * kSeedRowChunks];
   __shared__ uint4 urows[32 * kSeedRowChunks];
   __shared__ float lval[kSeedT];
   __shared__ int vt[kSeedT];
-  const int q = blockIdx.x, lane = threadIdx.x;
+  const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const int a = anchor[q];
-  float th;
-  if (seed_by_mfma(sa)) {
-    stage_seed_rows(sa, q * B, wrows, lval, vt, lane, 64);
-    stage_parent_rows(sa, anchor + q, 1, urows, lane, 64);
-    __syncthreads();
-    th = seed_theta_mfma(sa, wrows, urows, lval, vt, lane);
-  } else {
-    th = seed_theta(sa, a, q * B, lane);
-  }
   if (sa.upack != nullptr) {
     // packed U row of this parent (parent q of the depth-1 frontier)
     const int ch = sa.r / 8;
     const uint4* urow = reinterpret_cast<const uint4*>(sa.U) +
                         (int64_t)min(max(a, 0), sa.V - 1) * ch;
-    for (int c = lane; c < ch; c += 64)
+    for (int c = tid; c < ch; c += kInitThreads)
       sa.upack[upack_index(q, c, ch / 2)] = urow[c];
   }
+  const bool mf = seed_by_mfma(sa);
+  if (mf) {
+    stage_seed_rows(sa, q * B, wrows, lval, vt, tid, kInitThreads);
+    stage_parent_rows(sa, anchor + q, 1, urows, tid, kInitThreads);
+    __syncthreads();
+  }
+  if (tid >= 64) return;
+  const float th = mf ? seed_theta_mfma(sa, wrows, urows, lval, vt, lane)
+                      : seed_theta(sa, a, q * B, lane);
   if (lane == 0) {
     f.tok[q] = a;
     f.pid[q] = -1;
@@ -864,8 +866,8 @@ hipError_t launch_rowtop(const float* L, int rows, int V, int64_t lstride,
 
 hipError_t launch_init(int batch, int B, const int32_t* anchor, Frontier f,
                        int32_t* gcnt, const SeedArgs& sa, hipStream_t s) {
-  hipLaunchKernelGGL(init_kernel, dim3(batch), dim3(64), 0, s, B, anchor, f,
-                     gcnt, sa);
+  hipLaunchKernelGGL(init_kernel, dim3(batch), dim3(kInitThreads), 0, s, B,
+                     anchor, f, gcnt, sa);
   return hipGetLastError();
 }
 
