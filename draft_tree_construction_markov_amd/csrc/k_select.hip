@@ -7,6 +7,8 @@
 #include "pct_device.h"
 #include "pct_internal.h"
 
+#include <algorithm>
+
 namespace pct {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -764,75 +766,89 @@ __global__ __launch_bounds__(kExpandWaves * 64) void expand_kernel(
   }
 }
 
-// Global top-N of every generated child of one request, by key; parents
-// remapped to output indices.  Bitonic sort in LDS.
-__global__ __launch_bounds__(1024) void topn_kernel(TopNArgs a) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  int n2 = 1;
-  while (n2 < a.pool_n) n2 <<= 1;
-  uint64_t* key = reinterpret_cast<uint64_t*>(smem);
-  int16_t* id = reinterpret_cast<int16_t*>(smem + 8 * n2);
-  int16_t* inv = id + n2;
-  const int q = blockIdx.x, tid = threadIdx.x;
-  for (int i = tid; i < n2; i += 1024) {
-    key[i] = i < a.pool_n ? a.pool_key[(int64_t)q * a.pool_n + i]
-                          : ~(uint64_t)0;
-    id[i] = (int16_t)i;
-    inv[i] = -1;
-  }
-  __syncthreads();
-  // A stage with stride <= 32 pairs elements inside one 128-element block
-  // per wave (pair i of the wave's 64 touches 128*(i/64) .. +127), so the
-  // waves need no workgroup barrier between two such stages, only a wave
-  // fence; a stage with a larger stride is fenced by workgroup barriers.
-  for (int size = 2; size <= n2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < n2 / 2; i += 1024) {
-        const int lo = 2 * stride * (i / stride) + (i % stride);
-        const int hi = lo + stride;
-        const bool up = (lo & size) == 0;
-        const uint64_t kl = key[lo], kh = key[hi];
-        if ((kl > kh) == up) {
-          key[lo] = kh;
-          key[hi] = kl;
-          const int16_t t = id[lo];
-          id[lo] = id[hi];
-          id[hi] = t;
-        }
-      }
-      const int next = stride > 1 ? stride >> 1 : (2 * size <= n2 ? size : 0);
-      if (stride > 32 || next > 32 || next == 0) {
-        __syncthreads();
-      } else {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      }
+// Global top-N of every generated child of one request.  A key's output
+// position is its rank among the request's keys in (key asc, pool id asc):
+// the number of keys that come before it.  Keys are distinct except for
+// padding children (score -inf, token 0, same parent), so the pool-id term
+// is only counted for those.  Four lanes share a key, each counting over a
+// quarter of the keys (16-byte LDS reads, two keys each), and add their
+// counts with quad DPP; a kept key's parent index is the rank of the
+// parent's key, found the same way.  A request's keys are split over
+// several workgroups (blockIdx.x), so the whole chip takes part.
+constexpr int kTopNThreads = 256;
+
+__device__ __forceinline__ int quad_sum(int x) {
+  x += dpp_i<kDppXor1>(x);
+  x += dpp_i<kDppXor2>(x);
+  return x;
+}
+
+// Keys before `key` (pool id e) among the 2*npairs keys of k2 (the tail is
+// padded with ~0, above every key); lane `sub` of the quad takes pairs
+// sub, sub+4, ...  All four lanes of a quad call it with the same key.
+__device__ __forceinline__ int rank_of(const ulonglong2* k2, int npairs,
+                                       uint64_t key, int e, int sub) {
+  int r = 0;
+  // unrolled so that several LDS reads are in flight at once
+  if (key_score(key) != neg_inf()) {
+#pragma unroll 8
+    for (int j = sub; j < npairs; j += 4) {
+      const ulonglong2 v = k2[j];
+      r += (v.x < key) + (v.y < key);
+    }
+  } else {
+#pragma unroll 8
+    for (int j = sub; j < npairs; j += 4) {
+      const ulonglong2 v = k2[j];
+      r += (v.x < key) + (v.y < key) + (v.x == key && 2 * j < e) +
+           (v.y == key && 2 * j + 1 < e);
     }
   }
-  const int n = min(a.N, a.pool_n);
-  for (int i = tid; i < n; i += 1024) inv[id[i]] = (int16_t)i;
+  return quad_sum(r);
+}
+
+__global__ __launch_bounds__(kTopNThreads) void topn_kernel(TopNArgs a,
+                                                            int splits) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint64_t* key = reinterpret_cast<uint64_t*>(smem);
+  const ulonglong2* k2 = reinterpret_cast<const ulonglong2*>(smem);
+  const int q = blockIdx.y, sp = blockIdx.x, tid = threadIdx.x;
+  const int pn = a.pool_n, npairs = (pn + 1) / 2;
+  for (int i = tid; i < 2 * npairs; i += kTopNThreads)
+    key[i] = i < pn ? a.pool_key[(int64_t)q * pn + i] : ~(uint64_t)0;
   __syncthreads();
-  for (int i = tid; i < a.N; i += 1024) {
-    const int64_t o = (int64_t)q * a.N + i;
-    if (i < n) {
-      const uint64_t k = key[i];
-      const int pid = id[i];
+  const int n = min(a.N, pn);
+  const int per = (pn + splits - 1) / splits;
+  const int e0 = sp * per, e1 = min(e0 + per, pn);
+  const int grp = tid >> 2, sub = tid & 3;
+  for (int b0 = e0; b0 < e1; b0 += kTopNThreads / 4) {
+    const int e = b0 + grp;  // the same for the four lanes of a quad
+    if (e >= e1) continue;
+    const uint64_t k = key[e];
+    const int r = rank_of(k2, npairs, k, e, sub);
+    if (r >= n) continue;
+    const int pp = key_ppid(k);
+    const int pr = pp < 0 ? -1 : rank_of(k2, npairs, key[pp], pp, sub);
+    if (sub == 0) {
       int d = 1;
-      while (d < a.B && pid >= a.base[d + 1]) ++d;
-      const int pp = key_ppid(k);
+      while (d < a.B && e >= a.base[d + 1]) ++d;
+      const int64_t o = (int64_t)q * a.N + r;
       a.tok[o] = key_tok(k);
-      a.parent[o] = pp < 0 ? -1 : inv[pp];
+      a.parent[o] = pr;
       a.depth[o] = d;
       a.score[o] = key_score(k);
-    } else {
+    }
+  }
+  if (sp == 0) {
+    for (int i = n + tid; i < a.N; i += kTopNThreads) {
+      const int64_t o = (int64_t)q * a.N + i;
       a.tok[o] = -1;
       a.parent[o] = -1;
       a.depth[o] = 0;
       a.score[o] = neg_inf();
     }
+    if (tid == 0) a.n_nodes[q] = n;
   }
-  if (tid == 0) a.n_nodes[q] = n;
 }
 
 // Per-parent results of the standalone Markov-logit call.
@@ -877,18 +893,17 @@ hipError_t launch_expand(const ExpandArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-size_t topn_lds(int pool_n) {
-  int n2 = 1;
-  while (n2 < pool_n) n2 <<= 1;
-  return (size_t)n2 * 12;
-}
+size_t topn_lds(int pool_n) { return (size_t)((pool_n + 1) / 2) * 16; }
 
 hipError_t launch_topn(const TopNArgs& a, hipStream_t s) {
   hipError_t e = allow_lds(reinterpret_cast<const void*>(topn_kernel),
                            topn_lds(a.pool_n));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topn_kernel, dim3(a.batch), dim3(1024),
-                     topn_lds(a.pool_n), s, a);
+  // about 1024 workgroups over the batch, at least 64 keys each
+  int splits = (1024 + a.batch - 1) / a.batch;
+  splits = std::min(splits, std::max(1, (a.pool_n + 63) / 64));
+  hipLaunchKernelGGL(topn_kernel, dim3(splits, a.batch), dim3(kTopNThreads),
+                     topn_lds(a.pool_n), s, a, splits);
   return hipGetLastError();
 }
 
