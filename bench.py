@@ -17,6 +17,10 @@ Prints one JSON line (rank 0):
                (so that `value` is timed without events); `traffic` is the
                counted HBM bytes per launch from profiles/, or null when the
                kernel changed since the counters were taken
+  markov_memory_bound_depths
+               the fused kernel's launches at depths 1 and 2 (32 and 256
+               parents) against HBM peak: W once + the launch's L rows +
+               the parents' U rows, per launch
   cpu_baseline the CPU oracle on a bounded sample of the same workload
   adaptive     the adaptive best-first build (batch 64, n_max 1024) with its
                row-statistics kernels (single-read pieces, their merge and
@@ -186,6 +190,18 @@ def main():
     P_steady = w.batch * w.beam_w
     k1_ms, k1_n = pct.profile_read(pct.PROF_MARKOV, P_steady)
     k1_all_ms, k1_all_n = pct.profile_read(pct.PROF_MARKOV, -1)
+    # the memory-bound depths: 1 (the anchors, one parent per request) and
+    # 2 (the anchors' children that the beam keeps); algorithmic bytes =
+    # W once + the launch's L rows (one per request) + the parents' U rows
+    shallow = {}
+    for d, P in ((1, w.batch), (2, w.batch * min(w.k, w.beam_w))):
+        ms, nl = pct.profile_read(pct.PROF_MARKOV, P)
+        if nl:
+            byts = 2.0 * w.V * w.r + w.batch * 4.0 * w.V + P * 2.0 * w.r
+            gbs = byts / (ms / nl * 1e-3) / 1e9
+            shallow[f"depth{d}"] = {"parents": P, "avg_launch_ms": round(ms / nl, 5),
+                                    "bytes": int(byts), "achieved_GBs": round(gbs, 1),
+                                    "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
     kinds = {"markov": pct.PROF_MARKOV, "expand": pct.PROF_EXPAND,
              "topn": pct.PROF_TOPN, "mask": pct.PROF_MASK,
              "accept": pct.PROF_ACCEPT, "rowtop": pct.PROF_ROWTOP,
@@ -231,6 +247,7 @@ def main():
         "kernel_ms_per_step": per_kind,
         "markov_all_launches": {"ms_per_step": round(k1_all_ms / args.steps, 4),
                                 "launches_per_step": k1_all_n // args.steps},
+        "markov_memory_bound_depths": shallow,
         "mean_tau": float(np.mean(tau)),
         "roofline": roofline,
     }
