@@ -130,7 +130,7 @@ K1Plan plan_k1(int P, int V, int r, int k, int uw_dtype, bool has_uw,
       pl.NW = 8;
     }
     // static LDS: two W tiles and two L row buffers; dynamic: the lists
-    const size_t wbytes = (size_t)2 * 64 * 2 * R16 * 16;
+    const size_t wbytes = (size_t)2 * 64 * (2 * R16 + 1) * 16;  // padded rows
     auto slots_of = [&](int nw) {
       if (group_fp <= 0) return 0;
       const int span = nw * pl.NB * 32;

@@ -29,9 +29,14 @@ namespace pct {
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef const __attribute__((address_space(1))) void* gbl_ptr_t;
 
+// W tile layout in LDS: 64 rows of 2*R16 16-byte chunks, each row followed
+// by one pad chunk (row stride 2*R16 + 1 chunks).  The pad spreads the rows
+// of one MFMA operand read over all LDS banks, and chunk (row, c) sits at
+// row * stride + c, so a lane's reads of one tile differ only by immediate
+// offsets from one base address (no address register per rank step).
 template <int R16>
-__device__ __forceinline__ int wswz(int row, int c) {
-  return row * (2 * R16) + (c ^ (row & (2 * R16 - 1)));
+constexpr int wstride() {
+  return 2 * R16 + 1;
 }
 
 // Insert z (vocab v) into a lane's top-k list.  Within one lane the vocab
@@ -100,7 +105,8 @@ __device__ __forceinline__ void combine_halves(float& c2, float& s, int lane) {
 template <int NB, int NW, int R16, bool STAGED>
 __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
   constexpr int CH = 2 * R16;               // 16-byte chunks per W row
-  constexpr int TILE_CH = 64 * CH;          // chunks per 64-row tile
+  constexpr int RS = wstride<R16>();       // chunks per padded LDS row
+  constexpr int TILE_CH = 64 * RS;          // chunk slots per 64-row tile
   constexpr int SPAN = NW * NB * 32;        // parents per workgroup
   constexpr int LS = STAGED ? kLdsRowSlots : 4;
   // Double buffers as distinct LDS objects: the loop is unrolled by two so
@@ -175,9 +181,9 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
   }
 
   // Tile t -> LDS by direct global->LDS loads.  W: each wave instruction
-  // fills 64 consecutive 16-byte slots; slot q holds row q/CH, logical chunk
-  // (q%CH) ^ (row & (CH-1)), i.e. global chunk q ^ ((q/CH) & (CH-1)).  Rows
-  // past V are clamped to row V-1 (their outputs are masked).  L (staged):
+  // fills 64 consecutive 16-byte slots; slot q holds row q/RS, chunk q%RS
+  // (the pad chunk q%RS == CH receives a copy of the row's chunk 0, never
+  // read).  Rows past V are clamped to row V-1 (their outputs are masked).  L (staged):
   // 16 chunks per row slot; V % 4 == 0 here, so a chunk is inside the row or
   // wholly past V (then an in-bounds dummy that is never read).
   constexpr int LMAX = (LS * 16 + 64 * NW - 1) / (64 * NW);  // L DMAs/wave
@@ -202,10 +208,11 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
 #pragma unroll
     for (int gi = wave; gi < TILE_CH / 64; gi += NW) {
       const int q = gi * 64 + lane;
-      const int row = q / CH;
-      int off = q ^ (row & (CH - 1));
-      if (!wfull && 64 * t + row >= a.V)
-        off = (a.V - 1 - 64 * t) * CH + (off % CH);
+      int row = q / RS;
+      int c = q - row * RS;
+      c = c < CH ? c : 0;
+      if (!wfull && 64 * t + row >= a.V) row = a.V - 1 - 64 * t;
+      const int off = row * CH + c;
       __builtin_amdgcn_global_load_lds((gbl_ptr_t)(wbase + off),
                                        (lds_ptr_t)(wd + gi * 64), 16, 0, 0);
     }
@@ -221,24 +228,37 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
     }
   };
 
-  auto compute = [&](int t, const uint4* wt, const float4* lt) {
-    const bool full = 64 * t + 64 <= a.V;
+  f32x16 acc[NB];
+  // MFMA chain of half av of the tile in wt: acc[b] = W rows . U rows.  The
+  // A operand of step kk is chunk 2*kk + h of row 32*av + col; its reads run
+  // kRA steps ahead of the MFMAs that consume them.
+  const int wlane = col * RS + h;
+  auto mma = [&](const uint4* wt, int av) {
+    constexpr int kRA = R16 < 4 ? R16 : 4;
+    const uint4* wp = wt + wlane + 32 * RS * av;
 #pragma unroll
-    for (int av = 0; av < 2; ++av) {
-      f32x16 acc[NB];
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[b][j] = 0.f;
+    bf16x8 wf[kRA];
+#pragma unroll
+    for (int i = 0; i < kRA; ++i) wf[i] = __builtin_bit_cast(bf16x8, wp[2 * i]);
+#pragma unroll
+    for (int kk = 0; kk < R16; ++kk) {
+      const bf16x8 cur = wf[kk % kRA];
+      if (kk + kRA < R16)
+        wf[kk % kRA] = __builtin_bit_cast(bf16x8, wp[2 * (kk + kRA)]);
 #pragma unroll
       for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) acc[b][j] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < R16; ++kk) {
-        const bf16x8 wf =
-            __builtin_bit_cast(bf16x8, wt[wswz<R16>(32 * av + col, 2 * kk + h)]);
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, uf[b][kk],
-                                                          acc[b], 0, 0, 0);
-      }
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, uf[b][kk],
+                                                        acc[b], 0, 0, 0);
+    }
+  };
+  // Epilogue of half av of tile t (L rows of the tile in lt): z = L + acc,
+  // running max / exp-sum, rare top-k path.
+  auto epi = [&](int t, int av, const float4* lt) {
+    const bool full = 64 * t + 64 <= a.V;
+    {
       // register j of this lane holds vocab vb + 8*(j/4) + j%4
       const int vb = 64 * t + 32 * av + 4 * h;
 #pragma unroll
@@ -344,21 +364,43 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
     }
   };
 
+  // Two waves share each SIMD (waves w and w + NW/2).  The second half of
+  // the workgroup runs half a tile behind: while an early wave issues the
+  // MFMA chain of a half-tile, its SIMD partner runs the VALU epilogue of
+  // the previous one, so the matrix core and the VALU work at the same time
+  // instead of both waves contracting, then both exponentiating.  Per tile t:
+  //   early: mma(t,0) | epi(t,0) mma(t,1) epi(t,1)
+  //   late:  epi(t-1,1) | mma(t,0) epi(t,0) mma(t,1)
+  // The barrier at "|" follows the late waves' last read of tile t-1's L
+  // rows, so the loads of tile t+1 into that buffer are issued there; the
+  // barrier at the end of the tile waits for them.
+  const bool late = NW >= 2 && wave >= NW / 2;
+  auto tile = [&](int t, const uint4* wt, const float4* lt, uint4* wn,
+                  float4* ln, const float4* lp) {
+    if (!late) mma(wt, 0);
+    else if (t > t0) epi(t - 1, 1, lp);
+    __syncthreads();
+    if (t + 1 < t1) issue(t + 1, wn, ln);
+    if (!late) {
+      epi(t, 0, lt);
+      mma(wt, 1);
+      epi(t, 1, lt);
+    } else {
+      mma(wt, 0);
+      epi(t, 0, lt);
+      mma(wt, 1);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
   if (t0 < t1) issue(t0, w0, l0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   for (int t = t0; t < t1; t += 2) {
-    if (t + 1 < t1) issue(t + 1, w1, l1);
-    compute(t, w0, l0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (t + 1 < t1) {
-      if (t + 2 < t1) issue(t + 2, w0, l0);
-      compute(t + 1, w1, l1);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-    }
+    tile(t, w0, l0, w1, l1, l1);
+    if (t + 1 < t1) tile(t + 1, w1, l1, w0, l0, l0);
   }
+  if (late && t1 > t0) epi(t1 - 1, 1, ((t1 - 1 - t0) & 1) ? l1 : l0);
 
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
