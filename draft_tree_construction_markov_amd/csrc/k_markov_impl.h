@@ -253,6 +253,14 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
         acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, uf[b][kk],
                                                         acc[b], 0, 0, 0);
     }
+    // keep the schedule in that order: kRA reads first, then each step's
+    // MFMAs followed by the read kRA steps ahead
+    __builtin_amdgcn_sched_group_barrier(0x100, kRA, 0);  // LDS reads
+#pragma unroll
+    for (int kk = 0; kk < R16; ++kk) {
+      __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);  // MFMAs
+      if (kk + kRA < R16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
   };
   // Epilogue of half av of tile t (L rows of the tile in lt): z = L + acc,
   // running max / exp-sum, rare top-k path.
