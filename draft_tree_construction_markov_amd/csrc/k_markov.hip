@@ -21,6 +21,8 @@
 // staged through LDS (double-buffered, XOR-swizzled 16-byte chunks) and
 // shared by all waves of the workgroup.  A workgroup covers one slice of the
 // vocabulary for up to NB*NW*32 parents; slices x parent tiles form the grid.
+#include <algorithm>
+
 #include "k_markov_impl.h"
 
 namespace pct {
@@ -117,12 +119,11 @@ K1Plan plan_k1(int P, int V, int r, int k, int uw_dtype, bool has_uw,
   if (r_ok) {
     pl.kind = K1_MFMA;
     pl.R16 = R16;
-    if (P <= 32) {
-      pl.NB = 1;
-      pl.NW = 1;
-    } else if (P <= 256) {
+    if (P <= 256) {
       // 32 parents per wave, 8 waves: two waves share each SIMD (64 parents
-      // per wave would leave one)
+      // per wave would leave one).  Waves past the parents only load their
+      // share of each tile: with few parents the launch is bound by the
+      // tile loads, and eight waves issue them faster than one.
       pl.NB = 1;
       pl.NW = 8;
     } else {
@@ -133,7 +134,7 @@ K1Plan plan_k1(int P, int V, int r, int k, int uw_dtype, bool has_uw,
     const size_t wbytes = (size_t)2 * 64 * (2 * R16 + 1) * 16;  // padded rows
     auto slots_of = [&](int nw) {
       if (group_fp <= 0) return 0;
-      const int span = nw * pl.NB * 32;
+      const int span = std::min(nw * pl.NB * 32, P);
       return (span + group_fp - 1) / group_fp + 1;
     };
     auto lists_of = [&](int nw) {  // lists + their lengths

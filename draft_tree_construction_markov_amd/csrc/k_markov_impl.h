@@ -383,13 +383,18 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
   // rows, so the loads of tile t+1 into that buffer are issued there; the
   // barrier at the end of the tile waits for them.
   const bool late = NW >= 2 && wave >= NW / 2;
+  // a wave with no parents only loads its share of the tiles
+  const bool active = pw < a.P;
   auto tile = [&](int t, const uint4* wt, const float4* lt, uint4* wn,
                   float4* ln, const float4* lp) {
-    if (!late) mma(wt, 0);
-    else if (t > t0) epi(t - 1, 1, lp);
+    if (active) {
+      if (!late) mma(wt, 0);
+      else if (t > t0) epi(t - 1, 1, lp);
+    }
     __syncthreads();
     if (t + 1 < t1) issue(t + 1, wn, ln);
-    if (!late) {
+    if (!active) {
+    } else if (!late) {
       epi(t, 0, lt);
       mma(wt, 1);
       epi(t, 1, lt);
@@ -408,7 +413,8 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
     tile(t, w0, l0, w1, l1, l1);
     if (t + 1 < t1) tile(t + 1, w1, l1, w0, l0, l0);
   }
-  if (late && t1 > t0) epi(t1 - 1, 1, ((t1 - 1 - t0) & 1) ? l1 : l0);
+  if (active && late && t1 > t0)
+    epi(t1 - 1, 1, ((t1 - 1 - t0) & 1) ? l1 : l0);
 
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
