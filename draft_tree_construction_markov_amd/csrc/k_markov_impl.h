@@ -102,6 +102,19 @@ __device__ __forceinline__ void combine_halves(float& c2, float& s, int lane) {
   s = r;
 }
 
+// value of x in lane g of this lane's quad (a DPP quad_perm source operand)
+__device__ __forceinline__ float quad_bcast(float x, int g) {
+  const int xi = __builtin_bit_cast(int, x);
+  int r;
+  switch (g) {
+    case 0: r = __builtin_amdgcn_mov_dpp(xi, 0x00, 0xf, 0xf, true); break;
+    case 1: r = __builtin_amdgcn_mov_dpp(xi, 0x55, 0xf, 0xf, true); break;
+    case 2: r = __builtin_amdgcn_mov_dpp(xi, 0xaa, 0xf, 0xf, true); break;
+    default: r = __builtin_amdgcn_mov_dpp(xi, 0xff, 0xf, 0xf, true); break;
+  }
+  return __builtin_bit_cast(float, r);
+}
+
 template <int NB, int NW, int R16, bool STAGED>
 __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
   constexpr int CH = 2 * R16;               // 16-byte chunks per W row
@@ -136,6 +149,8 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
   const int nslots =
       STAGED ? (min(p0 + SPAN, a.P) - 1) / a.group_fp - g0 + 1 : 0;
 
+  // quads of lanes share one L row when groups are whole quads
+  const bool quadL = STAGED && (a.group_fp & 3) == 0 && (a.P & 3) == 0;
   bf16x8 uf[NB][R16];
   const float* lrow[NB];
   int lslot[NB];
@@ -187,7 +202,7 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
   // 16 chunks per row slot; V % 4 == 0 here, so a chunk is inside the row or
   // wholly past V (then an in-bounds dummy that is never read).
   constexpr int LMAX = (LS * 16 + 64 * NW - 1) / (64 * NW);  // L DMAs/wave
-  auto issue = [&](int t, uint4* wd, float4* ld) {
+  auto issue = [&](int t, uint4* wd, float4* ld) __attribute__((always_inline)) {
     // L sources first: any register reload happens before DMAs are in
     // flight, so it cannot make the wave wait for them
     const float* lsrc[LMAX];
@@ -233,7 +248,7 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
   // A operand of step kk is chunk 2*kk + h of row 32*av + col; its reads run
   // kRA steps ahead of the MFMAs that consume them.
   const int wlane = col * RS + h;
-  auto mma = [&](const uint4* wt, int av) {
+  auto mma = [&](const uint4* wt, int av) __attribute__((always_inline)) {
     constexpr int kRA = R16 < 4 ? R16 : 4;
     const uint4* wp = wt + wlane + 32 * RS * av;
 #pragma unroll
@@ -264,17 +279,37 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
   };
   // Epilogue of half av of tile t (L rows of the tile in lt): z = L + acc,
   // running max / exp-sum, rare top-k path.
-  auto epi = [&](int t, int av, const float4* lt) {
+  auto epi = [&](int t, int av, const float4* lt) __attribute__((always_inline)) {
     const bool full = 64 * t + 64 <= a.V;
     {
       // register j of this lane holds vocab vb + 8*(j/4) + j%4
       const int vb = 64 * t + 32 * av + 4 * h;
+      // one L float4 per lane and parent block, all read before the first
+      // block's adds
+      float4 lq[NB];
+      if (STAGED && full && quadL) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          lq[b] = lt[lslot[b] * 16 + 8 * av + h + 2 * (lane & 3)];
+      }
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         float z[16];
         if (STAGED) {
           const float4* lp = lt + lslot[b] * 16 + 8 * av + h;
-          if (full) {
+          if (full && quadL) {
+            // the four lanes of a quad hold four consecutive parents of one
+            // group, so they need the same 16 L values: each lane reads one
+            // float4 and the adds take the others from the quad's lanes
+            const float4 l4 = lq[b];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              z[4 * g + 0] = quad_bcast(l4.x, g) + acc[b][4 * g + 0];
+              z[4 * g + 1] = quad_bcast(l4.y, g) + acc[b][4 * g + 1];
+              z[4 * g + 2] = quad_bcast(l4.z, g) + acc[b][4 * g + 2];
+              z[4 * g + 3] = quad_bcast(l4.w, g) + acc[b][4 * g + 3];
+            }
+          } else if (full) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
               const float4 l4 = lp[2 * g];
@@ -349,6 +384,9 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
         }
         // rare path: some element may enter this lane's top-k.  A rolled
         // loop that shifts z keeps the code small; z is dead afterwards.
+        // Elements go to the list in vocabulary order (its tie rule needs
+        // it), and the loop ends after the last element at or above the
+        // threshold (which only rises as the list fills).
         const bool hit = m >= thr[b];
         if (__any(hit)) {
           if (hit) {
@@ -356,8 +394,11 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
             ZV* lst = lists + li * a.k;
             int cnt = lcount[li];
             int v = vb;
+            int jend = 0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) jend = z[i] >= thr[b] ? i + 1 : jend;
 #pragma unroll 1
-            for (int j = 0; j < 16; ++j) {
+            for (int j = 0; j < jend; ++j) {
               const float zj = z[0];
 #pragma unroll
               for (int i = 0; i < 15; ++i) z[i] = z[i + 1];
@@ -386,7 +427,7 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
   // a wave with no parents only loads its share of the tiles
   const bool active = pw < a.P;
   auto tile = [&](int t, const uint4* wt, const float4* lt, uint4* wn,
-                  float4* ln, const float4* lp) {
+                  float4* ln, const float4* lp) __attribute__((always_inline)) {
     if (active) {
       if (!late) mma(wt, 0);
       else if (t > t0) epi(t - 1, 1, lp);
