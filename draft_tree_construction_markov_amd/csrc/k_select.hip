@@ -38,6 +38,11 @@ __global__ __launch_bounds__(256) void row_top_kernel(const float* L, int V,
                                                        int32_t* rowtop) {
   __shared__ __align__(16) float sz[256];
   __shared__ __align__(16) int32_t sv[256];
+  __shared__ __align__(16) float cz[256 + 4];
+  __shared__ __align__(16) int32_t cv[256 + 4];
+  __shared__ float tau_z;
+  __shared__ int32_t tau_v;
+  __shared__ int wcount[4];
   const int row = blockIdx.x, piece = blockIdx.y, tid = threadIdx.x;
   const float* Lr = L + (int64_t)row * lstride;
   // piece bounds in tokens, a multiple of 4 apart so that vectors align
@@ -83,19 +88,69 @@ __global__ __launch_bounds__(256) void row_top_kernel(const float* L, int V,
   // slots without a distinct token (tiny pieces) stay -1 and are skipped
   int32_t* out = rowtop + (int64_t)row * kSeedT + piece * kRowTopSlots;
   if (tid < kRowTopSlots) out[tid] = -1;
+  if (tid == 0) {
+    tau_z = neg_inf();
+    tau_v = 0x7fffffff;
+  }
   __syncthreads();
-  // rank of the thread's best among the 256 (16-byte LDS reads, unrolled)
-  int rank = 0;
+  // The slots take the kRowTopSlots first of the 256 thread bests in
+  // (logit desc, token asc) order.  The kRowTopSlots-th of wave 0's 64
+  // entries is at or after the kRowTopSlots-th of all 256, so only entries
+  // at or before it can place; every entry before a candidate is itself a
+  // candidate, so a candidate's rank among the candidates is its rank among
+  // all.  (If wave 0 has fewer distinct entries, every entry is a
+  // candidate.)
   const float4* z4 = reinterpret_cast<const float4*>(sz);
   const int4* v4 = reinterpret_cast<const int4*>(sv);
-#pragma unroll 8
-  for (int j = 0; j < 64; ++j) {
-    const float4 z = z4[j];
-    const int4 v = v4[j];
-    rank += zv_before(z.x, v.x, bz, bv) + zv_before(z.y, v.y, bz, bv) +
+  if (tid < 64) {
+    int r0 = 0;
+#pragma unroll 4
+    for (int j = 0; j < 16; ++j) {
+      const float4 z = z4[j];
+      const int4 v = v4[j];
+      r0 += zv_before(z.x, v.x, bz, bv) + zv_before(z.y, v.y, bz, bv) +
             zv_before(z.z, v.z, bz, bv) + zv_before(z.w, v.w, bz, bv);
+    }
+    if (r0 == kRowTopSlots - 1) {  // equal entries carry equal values
+      tau_z = bz;
+      tau_v = bv;
+    }
   }
-  if (rank < kRowTopSlots && bv < V) out[rank] = bv;
+  __syncthreads();
+  const bool cand = !zv_before(tau_z, tau_v, bz, bv);
+  const uint64_t bal = __ballot(cand);
+  const int lane = tid & 63, wave = tid >> 6;
+  if (lane == 0) wcount[wave] = __popcll(bal);
+  __syncthreads();
+  int off = 0, m = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    off += w < wave ? wcount[w] : 0;
+    m += wcount[w];
+  }
+  if (cand) {
+    const int at = off + __popcll(bal & ((1ull << lane) - 1));
+    cz[at] = bz;
+    cv[at] = bv;
+  }
+  // pad to whole vectors with entries that come before nothing
+  if (tid < 4 && m + tid < 256 + 4) {
+    cz[m + tid] = neg_inf();
+    cv[m + tid] = 0x7fffffff;
+  }
+  __syncthreads();
+  if (cand) {
+    int rank = 0;
+    const float4* c4 = reinterpret_cast<const float4*>(cz);
+    const int4* d4 = reinterpret_cast<const int4*>(cv);
+    for (int j = 0; j < (m + 3) / 4; ++j) {
+      const float4 z = c4[j];
+      const int4 v = d4[j];
+      rank += zv_before(z.x, v.x, bz, bv) + zv_before(z.y, v.y, bz, bv) +
+              zv_before(z.z, v.z, bz, bv) + zv_before(z.w, v.w, bz, bv);
+    }
+    if (rank < kRowTopSlots && bv < V) out[rank] = bv;
+  }
 }
 
 __device__ __forceinline__ float dot_bf16(const uint16_t* u, const uint16_t* w,
