@@ -116,6 +116,18 @@ def test_large_frontier_parity(batch, B, V, k, beam, N, r, reqs):
     run_and_compare(L, U, W, A, k, beam, N, reqs=reqs)
 
 
+@pytest.mark.parametrize("batch,B,V,k,beam,N,r", [
+    (8, 4, 8192, 8, 16, 64, 256),     # frontiers of 128 parents, groups of 16
+    (32, 3, 4096, 8, 16, 64, 256),    # 512 parents: two blocks per wave
+])
+def test_flat_rows_many_candidates(batch, B, V, k, beam, N, r):
+    # flat logits put many elements of every row near the seed threshold, so
+    # the fused kernel's per-lane lists take many inserts; the groups are
+    # whole quads of lanes, which share their L values
+    L, U, W, A = _random(batch * 3 + V, batch, B, V, r, T=8.0)
+    run_and_compare(L, U, W, A, k, beam, N)
+
+
 def test_marginal_tree_parity():
     L, U, W, A = _random(7, 5, 6, 5000, 0)
     run_and_compare(L, U, W, A, 8, 16, 128)
