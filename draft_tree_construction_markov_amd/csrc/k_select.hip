@@ -828,7 +828,7 @@ __global__ __launch_bounds__(kExpandWaves * 64) void expand_kernel(
 // is only counted for those.  Four lanes share a key, each counting over a
 // quarter of the keys (16-byte LDS reads, two keys each), and add their
 // counts with quad DPP; a kept key's parent index is the rank of the
-// parent's key, found the same way.  A request's keys are split over
+// parent's key, counted in the same pass.  A request's keys are split over
 // several workgroups (blockIdx.x), so the whole chip takes part.
 constexpr int kTopNThreads = 256;
 
@@ -838,28 +838,33 @@ __device__ __forceinline__ int quad_sum(int x) {
   return x;
 }
 
-// Keys before `key` (pool id e) among the 2*npairs keys of k2 (the tail is
-// padded with ~0, above every key); lane `sub` of the quad takes pairs
-// sub, sub+4, ...  All four lanes of a quad call it with the same key.
-__device__ __forceinline__ int rank_of(const ulonglong2* k2, int npairs,
-                                       uint64_t key, int e, int sub) {
-  int r = 0;
-  // unrolled so that several LDS reads are in flight at once
-  if (key_score(key) != neg_inf()) {
+// Keys before ka (pool id ea) and before kb (pool id eb) among the 2*npairs
+// keys of k2 (the tail is padded with ~0, above every key), in one pass so
+// that every LDS read serves both counts; lane `sub` of the quad takes pairs
+// sub, sub+4, ...  All four lanes of a quad call it with the same keys.
+__device__ __forceinline__ void rank2_of(const ulonglong2* k2, int npairs,
+                                         uint64_t ka, int ea, uint64_t kb,
+                                         int eb, int sub, int& ra, int& rb) {
+  int x = 0, y = 0;
+  if (key_score(ka) != neg_inf() && key_score(kb) != neg_inf()) {
 #pragma unroll 8
     for (int j = sub; j < npairs; j += 4) {
       const ulonglong2 v = k2[j];
-      r += (v.x < key) + (v.y < key);
+      x += (v.x < ka) + (v.y < ka);
+      y += (v.x < kb) + (v.y < kb);
     }
   } else {
-#pragma unroll 8
+#pragma unroll 4
     for (int j = sub; j < npairs; j += 4) {
       const ulonglong2 v = k2[j];
-      r += (v.x < key) + (v.y < key) + (v.x == key && 2 * j < e) +
-           (v.y == key && 2 * j + 1 < e);
+      x += (v.x < ka) + (v.y < ka) + (v.x == ka && 2 * j < ea) +
+           (v.y == ka && 2 * j + 1 < ea);
+      y += (v.x < kb) + (v.y < kb) + (v.x == kb && 2 * j < eb) +
+           (v.y == kb && 2 * j + 1 < eb);
     }
   }
-  return quad_sum(r);
+  ra = quad_sum(x);
+  rb = quad_sum(y);
 }
 
 __global__ __launch_bounds__(kTopNThreads) void topn_kernel(TopNArgs a,
@@ -880,10 +885,14 @@ __global__ __launch_bounds__(kTopNThreads) void topn_kernel(TopNArgs a,
     const int e = b0 + grp;  // the same for the four lanes of a quad
     if (e >= e1) continue;
     const uint64_t k = key[e];
-    const int r = rank_of(k2, npairs, k, e, sub);
-    if (r >= n) continue;
+    // the key's rank and its parent's (the parent is the output row the
+    // node points to), counted together
     const int pp = key_ppid(k);
-    const int pr = pp < 0 ? -1 : rank_of(k2, npairs, key[pp], pp, sub);
+    int r, pr;
+    rank2_of(k2, npairs, k, e, pp < 0 ? k : key[pp], pp < 0 ? e : pp, sub, r,
+             pr);
+    if (r >= n) continue;
+    if (pp < 0) pr = -1;
     if (sub == 0) {
       int d = 1;
       while (d < a.B && e >= a.base[d + 1]) ++d;
