@@ -153,7 +153,7 @@ def main():
     def step():
         o = tb.run(dL, dU, dW, dA)
         pct.verify_accept(o.tok, o.parent, o.depth, o.n_nodes, dT, w.B,
-                          out=vout)
+                          out=vout, mask=o.mask)
 
     for _ in range(args.warmup):
         step()

@@ -65,7 +65,8 @@ def lib():
     L.pct_build_tree_workspace.argtypes = [C.POINTER(TreeShape)]
     L.pct_build_tree_workspace.restype = sz
     L.pct_tree_mask.argtypes = [i32, i32, P, P, P, P]
-    L.pct_verify_accept.argtypes = [i32, i32, i32, P, P, P, P, P, P, P, P, P]
+    L.pct_verify_accept.argtypes = [i32, i32, i32, P, P, P, P, P, P, P, P, P,
+                                    P]
     if hasattr(L, "pct_build_tree_adaptive"):
         L.pct_build_tree_adaptive.argtypes = [
             i32, i32, i32, i32, P, P, C.POINTER(CostModel), P, P, P, P, P, P,
@@ -324,8 +325,10 @@ def tree_mask(parent, n_nodes) -> torch.Tensor:
     return mask
 
 
-def verify_accept(tok, parent, depth, n_nodes, target, B: int, out=None):
-    """Greedy acceptance walk.  Returns (tau [batch], accept_node [batch][B],
+def verify_accept(tok, parent, depth, n_nodes, target, B: int, out=None,
+                  mask=None):
+    """Greedy acceptance walk; with the tree's packed ancestry mask the
+    acceptance test uses it.  Returns (tau [batch], accept_node [batch][B],
     accept_tok [batch][B+1])."""
     dev = _dev(tok)
     batch, N = (int(x) for x in tok.shape)
@@ -333,10 +336,13 @@ def verify_accept(tok, parent, depth, n_nodes, target, B: int, out=None):
         out = (torch.empty(batch, dtype=torch.int32, device=dev),
                torch.empty(batch, B, dtype=torch.int32, device=dev),
                torch.empty(batch, B + 1, dtype=torch.int32, device=dev))
+    if mask is not None and tuple(mask.shape) != (batch, N, (N + 63) // 64):
+        raise ValueError("mask must be [batch][N][ceil(N/64)]")
     tau, an, at = out
     _check(lib().pct_verify_accept(
         batch, N, B, _ptr(tok), _ptr(parent), _ptr(depth), _ptr(n_nodes),
-        _ptr(target), _ptr(tau), _ptr(an), _ptr(at), _stream(dev)))
+        _ptr(mask), _ptr(target), _ptr(tau), _ptr(an), _ptr(at),
+        _stream(dev)))
     return tau, an, at
 
 

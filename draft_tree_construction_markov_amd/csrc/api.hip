@@ -297,6 +297,10 @@ pct_status pct_build_tree(const pct_tree_shape* shape, const float* L,
   if (!U) sh.r = 0;
   else if (sh.r < 1)
     return fail(PCT_ERR_INVALID_ARG, "r must be >= 1 with Markov factors");
+  // the MFMA operand loads, the packed U rows and the seed dot products
+  // read the factors in 16-byte pieces
+  if (U && (!aligned16(U) || !aligned16(W)))
+    return fail(PCT_ERR_INVALID_ARG, "U and W must be 16-byte aligned");
   TreePlan tp;
   st = plan_tree(&sh, tp);
   if (st != PCT_OK) return st;
@@ -615,9 +619,9 @@ pct_status pct_tree_mask(int32_t batch, int32_t N, const int32_t* parent,
 pct_status pct_verify_accept(int32_t batch, int32_t N, int32_t B,
                              const int32_t* tok, const int32_t* parent,
                              const int32_t* depth, const int32_t* n_nodes,
-                             const int32_t* target, int32_t* tau,
-                             int32_t* accept_node, int32_t* accept_tok,
-                             void* stream) {
+                             const uint64_t* mask, const int32_t* target,
+                             int32_t* tau, int32_t* accept_node,
+                             int32_t* accept_tok, void* stream) {
   if (batch < 1 || N < 1 || B < 1 || N > 8192)
     return fail(PCT_ERR_INVALID_ARG, "need batch, B >= 1 and 1 <= N <= 8192");
   if (!tok || !parent || !depth || !n_nodes || !target || !tau ||
@@ -627,8 +631,8 @@ pct_status pct_verify_accept(int32_t batch, int32_t N, int32_t B,
   hipError_t e;
   {
     ProfScope ps(PROF_ACCEPT, batch, s);
-    e = launch_accept(batch, N, B, tok, parent, depth, n_nodes, target, tau,
-                      accept_node, accept_tok, s);
+    e = launch_accept(batch, N, B, tok, parent, depth, n_nodes, mask, target,
+                      tau, accept_node, accept_tok, s);
   }
   if (e != hipSuccess) return hip_fail(e, "accept kernel");
   return PCT_OK;

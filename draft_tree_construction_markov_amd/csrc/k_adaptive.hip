@@ -68,6 +68,7 @@ __global__ __launch_bounds__(kRowThreads) void rowsel_kernel(RowSelArgs a) {
   __shared__ float cz[kRowCap];
   __shared__ int cv[kRowCap];
   __shared__ float wm[kRowThreads / kWave];
+  __shared__ float wz[kRowThreads / kWave];
   __shared__ double ws[kRowThreads / kWave];
   __shared__ int s_count;
   __shared__ float s_tz;
@@ -122,8 +123,10 @@ __global__ __launch_bounds__(kRowThreads) void rowsel_kernel(RowSelArgs a) {
     const float sc = (m2 == neg_inf()) ? 0.f
                                        : S * __builtin_amdgcn_exp2f(m2 - wmax);
     const double wsum = wave_sum((double)sc);
+    const float wbest = wave_max(bz);
     if (lane == 0) {
       wm[wave] = wmax;
+      wz[wave] = wbest;
       ws[wave] = wsum;
     }
   }
@@ -139,9 +142,13 @@ __global__ __launch_bounds__(kRowThreads) void rowsel_kernel(RowSelArgs a) {
     float M = wm[0];
     for (int w = 1; w < kRowThreads / kWave; ++w) M = fmaxf(M, wm[w]);
     double tot = 0.0;
-    for (int w = 0; w < kRowThreads / kWave; ++w)
+    float zt = neg_inf();
+    for (int w = 0; w < kRowThreads / kWave; ++w) {
       if (wm[w] != neg_inf()) tot += ws[w] * exp2((double)wm[w] - M);
-    s_lse = (float)(kLn2 * ((double)M + log2(tot)));
+      zt = fmaxf(zt, wz[w]);
+    }
+    // never below the row maximum (see rowmerge_kernel)
+    s_lse = fmaxf((float)(kLn2 * ((double)M + log2(tot))), zt);
   }
 
   // bound: the K-th best of the group bests (K <= 256: groups of 4 threads)
@@ -503,12 +510,17 @@ __global__ __launch_bounds__(256) void rowmerge_kernel(RowMergeArgs a) {
   nvalid = wave_sum(nvalid);
   if ((tid & 63) == 0 && nvalid) atomicAdd(&s_valid, nvalid);
   if (tid == 0) {
-    float M = neg_inf();
-    for (int p = 0; p < a.parts; ++p) M = fmaxf(M, s_pm[p]);
+    float M = neg_inf(), zt = neg_inf();
+    for (int p = 0; p < a.parts; ++p) {
+      M = fmaxf(M, s_pm[p]);
+      zt = fmaxf(zt, mz[p * a.K]);  // each piece's best logit comes first
+    }
     double tot = 0.0;
     for (int p = 0; p < a.parts; ++p)
       if (s_pm[p] != neg_inf()) tot += s_ps[p] * exp2((double)s_pm[p] - M);
-    s_lse = (float)(kLn2 * ((double)M + log2(tot)));
+    // the row maximum bounds the log-normaliser from below; the log2-domain
+    // merge can land an ulp under it on a near one-hot row
+    s_lse = fmaxf((float)(kLn2 * ((double)M + log2(tot))), zt);
   }
   __syncthreads();
   const float lse = s_lse;

@@ -697,7 +697,10 @@ __global__ __launch_bounds__(kExpandWaves * 64) void expand_kernel(
       wave_topk_rank(a.gz + (int64_t)sp * a.cap, a.gv + (int64_t)sp * a.cap,
                      cnt, a.k, lane, pst + wave * kStageSlices,
                      [&](int i, float z, int32_t v) {
-                       const float l = z - lse;       // log pi(v|p)
+                       // log pi(v|p); the merged lse can land an ulp below
+                       // the row maximum on a near one-hot row, while the
+                       // true value is never positive
+                       const float l = fminf(z - lse, 0.f);
                        float s = sp_score + l;        // path score
                        s = s + 0.0f;                  // -0 -> +0
                        const int c = j * a.k + i;
@@ -923,10 +926,13 @@ __global__ __launch_bounds__(256) void finalize_kernel(
   const int lane = threadIdx.x & 63;
   const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (p >= P) return;
-  const float lse = wave_merge_lse(part_c, part_s, S, P, p, lane);
+  float lse = wave_merge_lse(part_c, part_s, S, P, p, lane);
   const int cnt = min(gcnt[p], cap);
   wave_topk(gz + (int64_t)p * cap, gv + (int64_t)p * cap, cnt, k, lane,
             [&](int i, float z, int32_t v) {
+              // the first result is the row maximum, a lower bound of the
+              // true log-normaliser (every lane sees the same values)
+              if (i == 0) lse = fmaxf(lse, z);
               if (lane == 0) {
                 topk_tok[(int64_t)p * k + i] = v;
                 topk_logp[(int64_t)p * k + i] = z - lse;

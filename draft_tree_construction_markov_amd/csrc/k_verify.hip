@@ -40,12 +40,19 @@ __global__ __launch_bounds__(256) void mask_kernel(int batch, int N,
 // target's token after its parent and every ancestor is accepted; accepted
 // nodes form a single root path (siblings have distinct tokens), whose
 // deepest node gives tau = depth + 1.
+// With the packed ancestry mask the test is one pass of word operations:
+// the nodes whose token matches form a bit set, and node i is accepted
+// exactly when its mask row (itself and its ancestors) lies inside that
+// set.  Without it, each node follows its parent links instead.
 __global__ __launch_bounds__(64) void accept_kernel(
     int N, int B, const int32_t* tok, const int32_t* parent,
-    const int32_t* depth, const int32_t* n_nodes, const int32_t* target,
-    int32_t* tau, int32_t* accept_node, int32_t* accept_tok) {
+    const int32_t* depth, const int32_t* n_nodes, const uint64_t* mask,
+    const int32_t* target, int32_t* tau, int32_t* accept_node,
+    int32_t* accept_tok) {
   extern __shared__ __align__(16) unsigned char smem[];
-  int32_t* par = reinterpret_cast<int32_t*>(smem);
+  const int words = (N + 63) / 64;
+  uint64_t* mbits = reinterpret_cast<uint64_t*>(smem);
+  int32_t* par = reinterpret_cast<int32_t*>(mbits + words);
   uint8_t* ok = reinterpret_cast<uint8_t*>(par + N);
   const int q = blockIdx.x, lane = threadIdx.x;
   const int n = min(n_nodes[q], N);
@@ -53,26 +60,41 @@ __global__ __launch_bounds__(64) void accept_kernel(
   const int32_t* Pa = parent + (int64_t)q * N;
   const int32_t* D = depth + (int64_t)q * N;
   const int32_t* tg = target + (int64_t)q * (N + 1);
-  for (int i = lane; i < n; i += kWave) {
-    const int p = Pa[i];
-    par[i] = p;
-    ok[i] = (p >= -1 && p < i) && T[i] == tg[p + 1];
+  // match bits, one word per 64 nodes (a whole wave per word)
+  for (int w = 0; w < words; ++w) {
+    const int i = 64 * w + lane;
+    bool m = false;
+    if (i < n) {
+      const int p = Pa[i];
+      par[i] = p;
+      m = (p >= -1 && p < i) && T[i] == tg[p + 1];
+      ok[i] = m;
+    }
+    const uint64_t b = __ballot(m);
+    if (lane == 0) mbits[w] = b;
   }
   __syncthreads();
   // deepest accepted node: key = depth * 2^20 + (2^20 - 1 - i)
   int best = -1;
   for (int i = lane; i < n; i += kWave) {
-    int a = i, steps = 0;
     bool acc = true;
-    while (a >= 0 && steps <= B) {
-      if (!ok[a]) {
-        acc = false;
-        break;
+    if (mask != nullptr) {
+      const uint64_t* row = mask + ((int64_t)q * N + i) * words;
+      for (int w = 0; w < words && acc; ++w) acc = (row[w] & ~mbits[w]) == 0;
+      acc = acc && ok[i];
+    } else {
+      int a = i, steps = 0;
+      while (a >= 0 && steps <= B) {
+        if (!ok[a]) {
+          acc = false;
+          break;
+        }
+        a = par[a];
+        ++steps;
       }
-      a = par[a];
-      ++steps;
+      acc = acc && a < 0;
     }
-    if (acc && a < 0) {
+    if (acc) {
       const int key = D[i] * (1 << 20) + ((1 << 20) - 1 - i);
       best = key > best ? key : best;
     }
@@ -115,12 +137,13 @@ hipError_t launch_mask(int batch, int N, const int32_t* parent,
 
 hipError_t launch_accept(int batch, int N, int B, const int32_t* tok,
                          const int32_t* parent, const int32_t* depth,
-                         const int32_t* n_nodes, const int32_t* target,
-                         int32_t* tau, int32_t* accept_node,
-                         int32_t* accept_tok, hipStream_t s) {
-  const size_t lds = (size_t)N * 5;
+                         const int32_t* n_nodes, const uint64_t* mask,
+                         const int32_t* target, int32_t* tau,
+                         int32_t* accept_node, int32_t* accept_tok,
+                         hipStream_t s) {
+  const size_t lds = (size_t)(N + 63) / 64 * 8 + (size_t)N * 5;
   hipLaunchKernelGGL(accept_kernel, dim3(batch), dim3(64), lds, s, N, B, tok,
-                     parent, depth, n_nodes, target, tau, accept_node,
+                     parent, depth, n_nodes, mask, target, tau, accept_node,
                      accept_tok);
   return hipGetLastError();
 }

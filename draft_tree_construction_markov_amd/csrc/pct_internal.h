@@ -198,8 +198,9 @@ hipError_t launch_mask(int batch, int N, const int32_t* parent,
                        const int32_t* n_nodes, uint64_t* mask, hipStream_t s);
 hipError_t launch_accept(int batch, int N, int B, const int32_t* tok,
                          const int32_t* parent, const int32_t* depth,
-                         const int32_t* n_nodes, const int32_t* target,
-                         int32_t* tau, int32_t* accept_node,
-                         int32_t* accept_tok, hipStream_t s);
+                         const int32_t* n_nodes, const uint64_t* mask,
+                         const int32_t* target, int32_t* tau,
+                         int32_t* accept_node, int32_t* accept_tok,
+                         hipStream_t s);
 
 }  // namespace pct

@@ -117,7 +117,8 @@ size_t pct_markov_logits_workspace(int32_t P, int32_t V, int32_t k);
  * frontier parent; the root's is -1.
  *
  *  L       [batch][B][V] fp32; row d-1 drives depth d
- *  U, W    [V][r] (W vocab-major) or both NULL (then z_d = L_d)
+ *  U, W    [V][r] (W vocab-major) or both NULL (then z_d = L_d); both
+ *          16-byte aligned
  *  anchor  [batch] root token of each request (the depth-1 parent)
  *  tok, parent, depth  [batch][N] int32 out; score [batch][N] fp32 out.
  *          Nodes come in key order, so parents precede children; parent is
@@ -126,9 +127,10 @@ size_t pct_markov_logits_workspace(int32_t P, int32_t V, int32_t k);
  *  n_nodes [batch] out: min(N, generated children)
  *  mask    [batch][N][ceil(N/64)] out, optional (NULL = not built)
  *  workspace  pct_build_tree_workspace(shape) bytes
- * Errors: as pct_markov_logits, plus PCT_ERR_UNSUPPORTED when the pool of
- * generated children per request exceeds 8192 or a per-depth candidate set
- * exceeds 2048. */
+ * Errors: as pct_markov_logits, plus PCT_ERR_INVALID_ARG for U or W not
+ * 16-byte aligned, and PCT_ERR_UNSUPPORTED when the pool of generated
+ * children per request exceeds 8192 or a per-depth candidate set exceeds
+ * 2048. */
 pct_status pct_build_tree(const pct_tree_shape* shape /*host*/,
                           const float* L, const void* U, const void* W,
                           const int32_t* anchor, int32_t* tok,
@@ -199,20 +201,25 @@ pct_status pct_tree_mask(int32_t batch, int32_t N, const int32_t* parent,
  *
  *  tok, parent, depth [batch][N] tree (parents precede children; siblings
  *          carry distinct tokens), n_nodes [batch]
+ *  mask    [batch][N][ceil(N/64)] optional: the tree's packed ancestry mask
+ *          (as pct_tree_mask writes it).  When given, a node is accepted
+ *          exactly when every node of its mask row matches, which replaces
+ *          the walk up the parent links by word operations; NULL = walk
  *  target  [batch][N+1]: target[0] is the target's token after the root,
  *          target[1+i] its token after node i
  *  tau     [batch] out: accepted tokens + 1 (the target's own token)
  *  accept_node [batch][B] out: the accepted nodes root-to-leaf, -1 padded
  *  accept_tok  [batch][B+1] out: their tokens, then the target's token,
  *          -1 padded
+ * Needs no workspace.
  * Errors: PCT_ERR_INVALID_ARG for batch < 1, N < 1, B < 1, N > 8192 or
- * null pointers. */
+ * null required pointers. */
 pct_status pct_verify_accept(int32_t batch, int32_t N, int32_t B,
                              const int32_t* tok, const int32_t* parent,
                              const int32_t* depth, const int32_t* n_nodes,
-                             const int32_t* target, int32_t* tau,
-                             int32_t* accept_node, int32_t* accept_tok,
-                             void* stream);
+                             const uint64_t* mask, const int32_t* target,
+                             int32_t* tau, int32_t* accept_node,
+                             int32_t* accept_tok, void* stream);
 
 /* ------------------------------------------------------------------------
  * Profiling (not from the pages; for measuring kernels against the

@@ -59,12 +59,16 @@ def load():
     lib.ref_pool_size.argtypes = [C.POINTER(TreeShape)]
     lib.ref_pool_size.restype = C.c_int64
     lib.ref_build_tree.argtypes = [C.POINTER(TreeShape), P, P, P, P, P, P, P,
-                                   P, P, P, P, P, P, P]
+                                   P, P, P, P, P, P, P, P]
     lib.ref_greedy_chain.argtypes = [i32, i32, i32, P, P, P, i32, i32, P]
     lib.ref_bestfirst.argtypes = [i32, i32, i32, P, P, P, i32, i32, i32, P, P,
                                   P, P, P, P]
-    lib.ref_adaptive.argtypes = [i32, i32, i32, P, i32, C.POINTER(CostModel),
-                                 P, P, P, P, P, P, P, P, P]
+    lib.ref_adaptive.argtypes = [i32, i32, i32, i32, P, P, P, i32, i32, i32,
+                                 C.POINTER(CostModel), P, P, P, P, P, P, P, P,
+                                 P]
+    lib.ref_stop.argtypes = [i32, P, i32, C.POINTER(CostModel), P, P, P, P]
+    lib.ref_throughput_curve.argtypes = [i32, P, i32, C.POINTER(CostModel),
+                                         P]
     lib.ref_mask.argtypes = [i32, i32, P, P]
     lib.ref_mask.restype = None
     lib.ref_accept.argtypes = [i32, i32, i32, P, P, P, P, P, P]
@@ -133,9 +137,10 @@ def pool_size(batch, B, V, r, k, beam_w, N) -> int:
 def build_tree(L, U, W, anchor, k: int, beam_w: int, N: int,
                diagnostics: bool = False):
     """PCTree on [batch][B][V] logits.  Returns a dict with tok, parent,
-    depth, score [batch][N], n_nodes [batch], min_gap [batch] and, with
-    diagnostics, pool_tok/pool_ppid/pool_score [batch][pool] and beam_pid
-    [batch][B][beam_w]."""
+    depth, score [batch][N], n_nodes [batch], min_gap [batch], depth_gap
+    [batch][B+1] (beam-boundary gap per depth, then the top-N boundary gap)
+    and, with diagnostics, pool_tok/pool_ppid/pool_score [batch][pool] and
+    beam_pid [batch][B][beam_w]."""
     L = _f32(L)
     batch, B, V = L.shape
     U, W, dt = _factors(U, W)
@@ -148,7 +153,8 @@ def build_tree(L, U, W, anchor, k: int, beam_w: int, N: int,
                depth=np.empty((batch, N), np.int32),
                score=np.empty((batch, N), np.float32),
                n_nodes=np.empty(batch, np.int32),
-               min_gap=np.empty(batch, np.float64))
+               min_gap=np.empty(batch, np.float64),
+               depth_gap=np.empty((batch, B + 1), np.float64))
     if diagnostics:
         out["pool_tok"] = np.empty((batch, pool), np.int32)
         out["pool_ppid"] = np.empty((batch, pool), np.int32)
@@ -160,7 +166,7 @@ def build_tree(L, U, W, anchor, k: int, beam_w: int, N: int,
         _p(out["parent"]), _p(out["depth"]), _p(out["score"]),
         _p(out["n_nodes"]), _p(out["min_gap"]), _p(out.get("pool_tok")),
         _p(out.get("pool_ppid")), _p(out.get("pool_score")),
-        _p(out.get("beam_pid")))
+        _p(out.get("beam_pid")), _p(out["depth_gap"]))
     _check(rc, "build_tree")
     return out
 
@@ -197,11 +203,21 @@ def bestfirst(L, U, W, anchor: int, n_max: int):
     return out
 
 
-def adaptive(L, n_max: int, ctx_len: int, cost: dict | None):
-    """One request's adaptive best-first tree ([B][V] marginal logits).
+def _cost(cost):
+    return None if cost is None else CostModel(cost["C_d"], cost["c0"],
+                                               cost["c1"], cost["c2"],
+                                               cost["c_ell"])
+
+
+def adaptive(L, n_max: int, ctx_len: int, cost: dict | None, U=None, W=None,
+             anchor: int = 0):
+    """One request's adaptive best-first tree ([B][V] logits): marginal rows
+    without U/W, parent-conditioned rows from `anchor` with them.
     cost: dict(C_d, c0, c1, c2, c_ell) or None for a fixed budget n_max."""
     L = _f32(L)
     B, V = L.shape
+    U, W, dt = _factors(U, W)
+    r = 0 if U is None else U.shape[1]
     out = dict(tok=np.empty(n_max, np.int32), parent=np.empty(n_max, np.int32),
                depth=np.empty(n_max, np.int32),
                score=np.empty(n_max, np.float32))
@@ -210,10 +226,9 @@ def adaptive(L, n_max: int, ctx_len: int, cost: dict | None):
     thr = np.empty(1, np.float64)
     g = np.empty(1, np.float64)
     gm = np.empty(1, np.float64)
-    cm = None if cost is None else CostModel(cost["C_d"], cost["c0"],
-                                             cost["c1"], cost["c2"],
-                                             cost["c_ell"])
-    rc = load().ref_adaptive(B, V, n_max, _p(L), int(ctx_len),
+    cm = _cost(cost)
+    rc = load().ref_adaptive(B, V, r, n_max, _p(L), _p(U), _p(W), dt,
+                             int(anchor), int(ctx_len),
                              None if cm is None else C.byref(cm),
                              _p(out["tok"]), _p(out["parent"]),
                              _p(out["depth"]), _p(out["score"]), _p(ns),
@@ -222,6 +237,33 @@ def adaptive(L, n_max: int, ctx_len: int, cost: dict | None):
     out.update(n_star=int(ns[0]), phi=float(phi[0]), throughput=float(thr[0]),
                min_gap=float(g[0]), gain_margin=float(gm[0]))
     return out
+
+
+def stop(score, n_avail: int, ctx_len: int, cost: dict | None):
+    """Throughput stop over best-first-ordered scores.  Returns dict with
+    n_star, phi, throughput, gain_margin."""
+    sc = _f32(score)
+    ns = np.empty(1, np.int32)
+    phi = np.empty(1, np.float64)
+    thr = np.empty(1, np.float64)
+    gm = np.empty(1, np.float64)
+    cm = _cost(cost)
+    _check(load().ref_stop(int(n_avail), _p(sc), int(ctx_len),
+                           None if cm is None else C.byref(cm), _p(ns),
+                           _p(phi), _p(thr), _p(gm)), "stop")
+    return dict(n_star=int(ns[0]), phi=float(phi[0]),
+                throughput=float(thr[0]), gain_margin=float(gm[0]))
+
+
+def throughput_curve(score, n_avail: int, ctx_len: int, cost: dict | None):
+    """f(n) = (1 + Phi_n) / D(n) for n = 0..n_avail."""
+    sc = _f32(score)
+    f = np.empty(int(n_avail) + 1, np.float64)
+    cm = _cost(cost)
+    _check(load().ref_throughput_curve(int(n_avail), _p(sc), int(ctx_len),
+                                       None if cm is None else C.byref(cm),
+                                       _p(f)), "throughput_curve")
+    return f
 
 
 def mask(parent, n_nodes: int, N: int) -> np.ndarray:

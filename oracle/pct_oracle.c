@@ -153,7 +153,8 @@ int ref_build_tree(const ref_tree_shape* sh, const float* L, const void* U,
                    const void* W, const int32_t* anchor, int32_t* tok,
                    int32_t* parent, int32_t* depth, float* score,
                    int32_t* n_nodes, double* min_gap, int32_t* pool_tok,
-                   int32_t* pool_ppid, float* pool_score, int32_t* beam_pid) {
+                   int32_t* pool_ppid, float* pool_score, int32_t* beam_pid,
+                   double* depth_gap) {
   if (!sh || !L || !anchor || !tok || !parent || !depth || !score || !n_nodes)
     return REF_EINVAL;
   const int32_t batch = sh->batch, B = sh->B, V = sh->V, r = sh->r,
@@ -220,8 +221,11 @@ int ref_build_tree(const ref_tree_shape* sh, const float* L, const void* U,
       memcpy(sorted, pool + base, sizeof(cand_t) * (size_t)nc);
       qsort(sorted, (size_t)nc, sizeof(cand_t), cmp_cand);
       int32_t nf2 = nc < Wb ? nc : Wb;
+      double bgap = INFINITY;
       for (int32_t i = 0; i < nf2 && i + 1 < nc; ++i)
-        gap_update(&gap, sorted[i].s, sorted[i + 1].s);
+        gap_update(&bgap, sorted[i].s, sorted[i + 1].s);
+      if (bgap < gap) gap = bgap;
+      if (depth_gap) depth_gap[(int64_t)q * (B + 1) + (d - 1)] = bgap;
       memcpy(front, sorted, sizeof(cand_t) * (size_t)nf2);
       if (beam_pid) {
         int32_t* bp = beam_pid + ((int64_t)q * B + (d - 1)) * Wb;
@@ -242,8 +246,11 @@ int ref_build_tree(const ref_tree_shape* sh, const float* L, const void* U,
     memcpy(sorted, pool, sizeof(cand_t) * (size_t)pool_n);
     qsort(sorted, (size_t)pool_n, sizeof(cand_t), cmp_cand);
     int32_t n = pool_n < N ? (int32_t)pool_n : N;
+    double tgap = INFINITY;
     for (int32_t i = 0; i < n && i + 1 < pool_n; ++i)
-      gap_update(&gap, sorted[i].s, sorted[i + 1].s);
+      gap_update(&tgap, sorted[i].s, sorted[i + 1].s);
+    if (tgap < gap) gap = tgap;
+    if (depth_gap) depth_gap[(int64_t)q * (B + 1) + B] = tgap;
     for (int64_t i = 0; i < pool_n; ++i) inv[i] = -1;
     for (int32_t i = 0; i < n; ++i) inv[sorted[i].id] = i;
     for (int32_t i = 0; i < N; ++i) {
@@ -487,28 +494,21 @@ static double round_cost(const ref_cost_model* c, double n, double ell) {
 }
 
 /* [CAD] "Method": maximise (1 + Phi(T_n)) / (C_d + C_v(n; l)) over the
- * best-first trees T_n; nodes are added in order and the build stops as soon
- * as the marginal gain of the next node is not positive.  The gain of node
- * n+1 has the sign of f(n+1) - f(n), i.e. of
- * P_{n+1} D(n) - (1 + Phi_n)(D(n+1) - D(n)). */
-int ref_adaptive(int32_t B, int32_t V, int32_t n_max, const float* L,
-                 int32_t ctx_len, const ref_cost_model* cost, int32_t* tok,
-                 int32_t* parent, int32_t* depth, float* score,
-                 int32_t* n_star, double* phi, double* throughput,
-                 double* min_gap, double* gain_margin) {
-  if (!n_star || !phi || !throughput || n_max < 1) return REF_EINVAL;
-  int32_t n_avail = 0;
-  double gap = INFINITY, order_gap;
-  int rc = ref_bestfirst(B, V, 0, L, NULL, NULL, REF_F32, 0, n_max, tok,
-                         parent, depth, score, &n_avail, &order_gap);
-  if (rc) return rc;
+ * trees T_n of the first n nodes of a best-first order; nodes are added in
+ * order and the build stops as soon as the marginal gain of the next node
+ * is not positive.  The gain of node n+1 has the sign of f(n+1) - f(n),
+ * i.e. of P_{n+1} D(n) - (1 + Phi_n)(D(n+1) - D(n)). */
+int ref_stop(int32_t n_avail, const float* score, int32_t ctx_len,
+             const ref_cost_model* cost, int32_t* n_star, double* phi,
+             double* throughput, double* gain_margin) {
+  if (!n_star || !phi || !throughput || n_avail < 0 ||
+      (n_avail > 0 && !score))
+    return REF_EINVAL;
   int32_t ns = n_avail;
   double margin = INFINITY;
-  double Phi = 0.0;
   if (cost) {
     const double ell = (double)ctx_len;
     double run = 0.0;
-    ns = n_avail;
     for (int32_t n = 0; n < n_avail; ++n) {
       double P1 = exp((double)score[n]); /* P_{n+1} (score index n) */
       double Dn = round_cost(cost, (double)n, ell);
@@ -527,7 +527,53 @@ int ref_adaptive(int32_t B, int32_t V, int32_t n_max, const float* L,
       run += P1;
     }
   }
+  double Phi = 0.0;
   for (int32_t i = 0; i < ns; ++i) Phi += exp((double)score[i]);
+  *n_star = ns;
+  *phi = Phi;
+  /* without a cost model the throughput is reported as 1 + Phi */
+  *throughput =
+      (1.0 + Phi) / (cost ? round_cost(cost, (double)ns, (double)ctx_len)
+                          : 1.0);
+  if (gain_margin) *gain_margin = margin;
+  return REF_OK;
+}
+
+/* [CAD] "Method": the throughput of the tree of the first n nodes,
+ * f(n) = (1 + Phi_n) / D(n), for every n = 0..n_avail (Phi_n summed in
+ * order, in double; D = 1 without a cost model). */
+int ref_throughput_curve(int32_t n_avail, const float* score, int32_t ctx_len,
+                         const ref_cost_model* cost, double* f) {
+  if (!f || n_avail < 0 || (n_avail > 0 && !score)) return REF_EINVAL;
+  double Phi = 0.0;
+  for (int32_t n = 0; n <= n_avail; ++n) {
+    const double D =
+        cost ? round_cost(cost, (double)n, (double)ctx_len) : 1.0;
+    f[n] = (1.0 + Phi) / D;
+    if (n < n_avail) Phi += exp((double)score[n]);
+  }
+  return REF_OK;
+}
+
+/* [CAD] "Method" on the best-first tree: over a block-diffusion drafter's
+ * marginals (U, W NULL) or over the parent-conditioned rows of [PCT]
+ * "straight draft" (U, W given, the first parent being the anchor). */
+int ref_adaptive(int32_t B, int32_t V, int32_t r, int32_t n_max,
+                 const float* L, const void* U, const void* W,
+                 int32_t uw_dtype, int32_t anchor, int32_t ctx_len,
+                 const ref_cost_model* cost, int32_t* tok, int32_t* parent,
+                 int32_t* depth, float* score, int32_t* n_star, double* phi,
+                 double* throughput, double* min_gap, double* gain_margin) {
+  if (!n_star || !phi || !throughput || n_max < 1) return REF_EINVAL;
+  int32_t n_avail = 0;
+  double gap = INFINITY, order_gap;
+  int rc = ref_bestfirst(B, V, r, L, U, W, uw_dtype, anchor, n_max, tok,
+                         parent, depth, score, &n_avail, &order_gap);
+  if (rc) return rc;
+  rc = ref_stop(n_avail, score, ctx_len, cost, n_star, phi, throughput,
+                gain_margin);
+  if (rc) return rc;
+  const int32_t ns = *n_star;
   /* gaps that decide the kept prefix: adjacent scores up to node n*+1 */
   for (int32_t i = 0; i + 1 < n_avail && i <= ns; ++i)
     gap_update(&gap, score[i], score[i + 1]);
@@ -537,15 +583,7 @@ int ref_adaptive(int32_t B, int32_t V, int32_t n_max, const float* L,
     depth[i] = 0;
     score[i] = -INFINITY;
   }
-  *n_star = ns;
-  *phi = Phi;
-  {
-    /* without a cost model the throughput is reported as 1 + Phi */
-    double D = cost ? round_cost(cost, (double)ns, (double)ctx_len) : 1.0;
-    *throughput = (1.0 + Phi) / D;
-  }
   if (min_gap) *min_gap = gap;
-  if (gain_margin) *gain_margin = margin;
   return REF_OK;
 }
 

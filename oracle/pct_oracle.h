@@ -79,12 +79,16 @@ int64_t ref_pool_size(const ref_tree_shape* sh);
  * (-1 = root); pads beyond n_nodes: tok -1, parent -1, depth 0, score -inf.
  * Optional diagnostics: min_gap [batch]; pool_* [batch][pool] (the generated
  * candidates by pool id); beam_pid [batch][B][beam_w] (the expanded frontier
- * of every depth by pool id, -2 padded). */
+ * of every depth by pool id, -2 padded); depth_gap [batch][B+1]: entry d-1
+ * the smallest score gap between adjacent candidates among the first
+ * beam_w+1 of depth d (the beam boundary), entry B the same over the first
+ * N+1 of the pool (the global top-N). */
 int ref_build_tree(const ref_tree_shape* sh, const float* L, const void* U,
                    const void* W, const int32_t* anchor, int32_t* tok,
                    int32_t* parent, int32_t* depth, float* score,
                    int32_t* n_nodes, double* min_gap, int32_t* pool_tok,
-                   int32_t* pool_ppid, float* pool_score, int32_t* beam_pid);
+                   int32_t* pool_ppid, float* pool_score, int32_t* beam_pid,
+                   double* depth_gap);
 
 /* Greedy chain of the Markov-head drafter: y_0 = anchor,
  * y_d = argmax_v z_d(y_{d-1}) (lowest token on ties). */
@@ -105,18 +109,33 @@ int ref_bestfirst(int32_t B, int32_t V, int32_t r, const float* L,
                   int32_t* parent, int32_t* depth, float* score,
                   int32_t* n_out, double* min_gap);
 
-/* Adaptive budget on the marginal best-first order: P_i = exp(s_i),
- * Phi_n = sum_{i<=n} P_i, D(n) = C_d + C_v(n; l),
+/* Throughput stop over an ordered list of prefix scores (a best-first
+ * order): P_i = exp(s_i), Phi_n = sum_{i<=n} P_i, D(n) = C_d + C_v(n; l),
  * g(n) = P_{n+1} D(n) - (1 + Phi_n)(D(n+1) - D(n)); n* is the first n with
- * g(n) <= 0 (n* = number of available nodes if none; cost NULL => n_max).
- * Writes the first n* nodes (pads as in ref_build_tree), n*, Phi(n*) and the
- * throughput (1 + Phi)/D(n*).  gain_margin (optional) receives
- * min over n in {n*-1, n*} of |g(n)| / max(P_{n+1} D(n), (1+Phi_n) dD(n)). */
-int ref_adaptive(int32_t B, int32_t V, int32_t n_max, const float* L,
-                 int32_t ctx_len, const ref_cost_model* cost, int32_t* tok,
-                 int32_t* parent, int32_t* depth, float* score,
-                 int32_t* n_star, double* phi, double* throughput,
-                 double* min_gap, double* gain_margin);
+ * g(n) <= 0 (n_avail if none; cost NULL => n_avail).  Outputs n*,
+ * Phi(n*), the throughput (1 + Phi)/D(n*) (1 + Phi without a cost model)
+ * and, optionally, gain_margin = min over n in {n*-1, n*} of
+ * |g(n)| / max(P_{n+1} D(n), (1+Phi_n) dD(n)). */
+int ref_stop(int32_t n_avail, const float* score, int32_t ctx_len,
+             const ref_cost_model* cost, int32_t* n_star, double* phi,
+             double* throughput, double* gain_margin);
+
+/* f(n) = (1 + Phi_n) / D(n) for n = 0..n_avail (f has n_avail + 1
+ * entries; D = 1 without a cost model). */
+int ref_throughput_curve(int32_t n_avail, const float* score, int32_t ctx_len,
+                         const ref_cost_model* cost, double* f);
+
+/* Adaptive best-first tree: ref_bestfirst (marginal rows when U/W are NULL,
+ * parent-conditioned rows from the anchor otherwise) followed by ref_stop.
+ * Writes the first n* nodes (pads as in ref_build_tree), n*, Phi(n*), the
+ * throughput, and optionally the smallest adjacent score gap up to node
+ * n*+1 (min_gap) and the gain margin. */
+int ref_adaptive(int32_t B, int32_t V, int32_t r, int32_t n_max,
+                 const float* L, const void* U, const void* W,
+                 int32_t uw_dtype, int32_t anchor, int32_t ctx_len,
+                 const ref_cost_model* cost, int32_t* tok, int32_t* parent,
+                 int32_t* depth, float* score, int32_t* n_star, double* phi,
+                 double* throughput, double* min_gap, double* gain_margin);
 
 /* Packed ancestry mask of one tree: row i holds bit i and every bit of its
  * ancestors; words per row = ceil(N/64), bit j%64 of word j/64; rows >= n

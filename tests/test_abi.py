@@ -97,8 +97,12 @@ def test_adaptive_rejects_bad_arguments():
 def test_verify_and_mask_reject_bad_arguments():
     lib = pct.lib()
     d = C.c_void_p(16)
-    assert lib.pct_verify_accept(0, 4, 2, d, d, d, d, d, d, d, d, None) == 1
-    assert lib.pct_verify_accept(1, 9000, 2, d, d, d, d, d, d, d, d,
+    assert lib.pct_verify_accept(0, 4, 2, d, d, d, d, None, d, d, d, d,
+                                 None) == 1
+    assert lib.pct_verify_accept(1, 9000, 2, d, d, d, d, d, d, d, d, d,
+                                 None) == 1
+    # the mask is optional; the target is not
+    assert lib.pct_verify_accept(1, 4, 2, d, d, d, d, d, None, d, d, d,
                                  None) == 1
     assert lib.pct_tree_mask(1, 0, d, d, d, None) == 1
     assert lib.pct_tree_mask(1, 4, None, d, d, None) == 1
@@ -116,3 +120,18 @@ def test_markov_logits_rejects_bad_arguments():
     # workspace too small
     assert lib.pct_markov_logits(d, 100, 1, d, d, 1, 100, 32, d, d, 4, 8, d,
                                  d, d, None, d, 16, None) == 3
+
+
+def test_build_tree_rejects_unaligned_factors():
+    # a factor view at an element offset would feed misaligned 16-byte
+    # loads to the kernels: rejected on the host, nothing enqueued
+    lib = pct.lib()
+    sh = _shape(r=32, uw_dtype=1)
+    need = lib.pct_build_tree_workspace(C.byref(sh))
+    d = C.c_void_p(256)
+    odd = C.c_void_p(256 + 2)
+    for U, W in ((odd, d), (d, odd)):
+        rc = lib.pct_build_tree(C.byref(sh), d, U, W, d, d, d, d, d, d, None,
+                                d, need, None)
+        assert rc == 1
+        assert b"aligned" in lib.pct_last_error()

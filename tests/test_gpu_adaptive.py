@@ -12,11 +12,51 @@ import draft_tree_construction_markov_amd as pct
 import oracle
 import synth
 from gpu_util import announce, dev_f32, dev_i32
-from treecheck import NEAR_TIE, SCORE_TOL, check_structure
+from treecheck import NEAR_TIE, SCORE_TOL, check_structure, path_tokens
 
 pytestmark = pytest.mark.gpu
 
 COST = {k: synth.ADAPTIVE[k] for k in ("C_d", "c0", "c1", "c2", "c_ell")}
+
+
+def _true_scores(L, tok, parent, n):
+    """Double-precision path log-probabilities of a best-first tree over
+    marginal rows (each edge: z - lse of its depth's row)."""
+    lse = [oracle.row_stats(L[d], None, 1)[0] for d in range(L.shape[0])]
+    out = []
+    for i in range(n):
+        p = int(parent[i])
+        d = 0 if p < 0 else len(path_tokens(tok, parent, p))
+        s = (0.0 if p < 0 else out[p]) + float(L[d][int(tok[i])]) - lse[d]
+        out.append(s)
+    return out
+
+
+def _near_ok(g, o, q, L, B):
+    """A request whose GPU tree differs from the oracle's: the first
+    difference must sit at an oracle near-tie (an ordering tie of the two
+    nodes there, or a stop decision whose gain is within 1e-4 relative of
+    zero), and the GPU tree must be valid: structure, scores equal to their
+    recomputation within 1e-4, and Phi within n * 1e-5 * max P of the
+    oracle's (the best-first tree maximises Phi for its size)."""
+    ns, no = int(g["n_star"][q]), o["n_star"]
+    check_structure(g["tok"][q], g["parent"][q], g["depth"][q], ns, B)
+    ts = _true_scores(L[q], g["tok"][q], g["parent"][q], ns)
+    for i in range(ns):
+        assert abs(ts[i] - float(g["score"][q][i])) < SCORE_TOL, (q, i)
+    if ns != no:
+        assert o["gain_margin"] < 1e-4, (q, ns, no, o["gain_margin"])
+    m = min(ns, no)
+    diff = [i for i in range(m)
+            if (g["tok"][q][i], g["parent"][q][i]) !=
+            (o["tok"][i], o["parent"][i])]
+    if diff:
+        i = diff[0]
+        assert abs(ts[i] - float(o["score"][i])) < NEAR_TIE, (q, i)
+        phi_g = sum(math.exp(x) for x in ts[:m])
+        phi_o = sum(math.exp(float(x)) for x in o["score"][:m])
+        maxP = math.exp(max(float(o["score"][0]), ts[0]))
+        assert phi_g >= phi_o - m * NEAR_TIE * maxP, (q, phi_g, phi_o)
 
 
 def run_compare(L, ctx, n_max, cost, label):
@@ -44,21 +84,54 @@ def run_compare(L, ctx, n_max, cost, label):
                 1e-4 * o["throughput"]
             bins["exact"] += 1
         else:
-            near = o["min_gap"] < NEAR_TIE or o["gain_margin"] < 1e-4
-            assert near, (q, ns, o["n_star"])
-            check_structure(g["tok"][q], g["parent"][q], g["depth"][q], ns, B)
+            _near_ok(g, o, q, L, B)
+            print(f"{label}: request {q} near-tie (n* {ns} vs {o['n_star']})")
             bins["near"] += 1
         want = oracle.mask(g["parent"][q], max(ns, 0), n_max)
         assert np.array_equal(g["mask"][q], want), q
-    print(f"{label}: bins {bins}, n* {list(g['n_star'][:16])}")
+    print(f"{label}: bins {bins}, n* {[int(x) for x in g['n_star'][:16]]}")
     return g, bins
 
 
-def test_adaptive_workload_sample():
+def test_adaptive_workload_full():
+    # the adaptive workload at full size, every request against the oracle
     a = synth.ADAPTIVE
-    L, peaked, ctx = synth.adaptive_round(a["seed"], 16, a["B"], a["V"])
-    g, bins = run_compare(L, ctx, a["n_max"], COST, "b16-adaptive")
-    assert bins["exact"] >= 14
+    L, peaked, ctx = synth.adaptive_round(a["seed"], a["batch"], a["B"],
+                                          a["V"])
+    g, bins = run_compare(L, ctx, a["n_max"], COST, "adaptive")
+    assert bins["exact"] + bins["near"] == a["batch"]
+    assert bins["near"] <= a["batch"] // 16, bins
+
+
+def test_sibling_score_tie_takes_the_larger_logit():
+    # two siblings whose fp32 scores tie exactly while their logits differ
+    # (tokens 1 < 2 carry logits 0.0010000 < 0.0010001 next to a logit of
+    # 20): the more probable one, token 2, is taken first
+    row = np.full(6, -50.0, np.float32)
+    row[3] = 20.0
+    row[1] = np.float32(0.0010000)
+    row[2] = np.float32(0.0010001)
+    L = np.stack([row, row])[None]
+    g, bins = run_compare(L, np.array([0], np.int32), 42, None, "sibling-tie")
+    d1 = [int(t) for t, p in zip(g["tok"][0], g["parent"][0]) if p == -1]
+    assert d1.index(2) < d1.index(1)
+
+
+def test_near_one_hot_rows():
+    # log-probability rows with a top-1 probability above 1 - 1e-7: every
+    # log pi stays <= 0, so children never outscore their parents
+    rng = np.random.default_rng(43)
+    V = 4000
+    rest = rng.normal(size=(3, 4, V)) - 24.0
+    rest[:, :, 17] = 0.0
+    m = rest.max(axis=2, keepdims=True)
+    L = (rest - (m + np.log(np.exp(rest - m).sum(axis=2,
+                                                  keepdims=True)))).astype(
+        np.float32)
+    g, bins = run_compare(L, np.full(3, 600, np.int32), 64, None, "one-hot")
+    assert np.all(g["score"][:, :64] <= 0.0)
+    g, bins = run_compare(L, np.full(3, 600, np.int32), 64, COST,
+                          "one-hot-cost")
 
 
 def test_fixed_budget_uses_full_lists():

@@ -7,6 +7,7 @@ oracle saw an fp32 gap below 1e-5 at a selection boundary or between two
 adjacent nodes, in which case the GPU tree must still be a valid tree whose
 scores are the oracle's path scores; FAIL otherwise."""
 import math
+import os
 
 import numpy as np
 import pytest
@@ -16,31 +17,46 @@ import draft_tree_construction_markov_amd as pct
 import oracle
 import synth
 from gpu_util import announce, dev_f32, dev_factors, dev_i32
-from treecheck import (NEAR_TIE, SCORE_TOL, check_structure, compare_trees,
-                       naive_accept, path_tokens)
+from parity import RequestContext, classify
+from treecheck import check_structure, naive_accept
 
 pytestmark = pytest.mark.gpu
 
 
-def _path_score(L, U, W, anchor, toks):
-    prev, s = int(anchor), 0.0
-    for d, v in enumerate(toks, start=1):
-        z = L[d - 1].astype(np.float64)
-        if U is not None:
-            z = z + oracle.markov_row(U, W, prev).astype(np.float64)
-        m = z.max()
-        s += z[v] - (m + math.log(np.exp(z - m).sum()))
-        prev = v
-    return s
+def _golden(name):
+    """The oracle's trees for every request of a full-size workload
+    (written by tests/golden/make_golden.py from the oracle alone)."""
+    path = os.path.join(os.path.dirname(__file__), "golden",
+                        f"{name}_trees.npz")
+    z = np.load(path)
+    w = synth.TREE_WORKLOADS[name]
+    assert list(z["shape"]) == [w.seed, w.batch, w.B, w.V, w.k, w.beam_w,
+                                w.N, w.r], "golden file is for another shape"
+    return {k: z[k] for k in z.files if k != "shape"}
 
 
-def _valid_near_tie(g, q, L, U, W, A, B):
-    n = int(g["n_nodes"][q])
-    check_structure(g["tok"][q], g["parent"][q], g["depth"][q], n, B)
-    for i in range(n):
-        toks = path_tokens(g["tok"][q], g["parent"][q], i)
-        s = _path_score(L[q], U, W, A[q], toks)
-        assert abs(s - float(g["score"][q][i])) < SCORE_TOL
+def compare_all(g, o, L, U, W, A, k, beam_w, N, reqs, mask=True):
+    """Bin every request of reqs (rows j of o correspond to requests
+    reqs[j]); FAIL raises."""
+    bins = {"exact": 0, "near": 0}
+    worst = 0.0
+    for j, q in enumerate(reqs):
+        gq = {k2: g[k2][[q]] for k2 in ("tok", "parent", "depth", "score",
+                                         "n_nodes")}
+        oq = {k2: o[k2][[j]] for k2 in ("tok", "parent", "depth", "score",
+                                         "n_nodes")}
+        ctx = RequestContext(L[q], U, W, A[q], k, beam_w, N)
+        res, det = classify(gq, oq, 0, ctx)
+        bins[res] += 1
+        if res == "exact":
+            worst = max(worst, det)
+        else:
+            print(f"request {q}: near-tie ({det})")
+        if mask:
+            want = oracle.mask(g["parent"][q], int(g["n_nodes"][q]), N)
+            assert np.array_equal(g["mask"][q], want), q
+    print(f"bins {bins}, max |dscore| {worst:.2e}")
+    return bins
 
 
 def run_and_compare(L, U, W, A, k, beam_w, N, reqs=None, mask=True):
@@ -54,23 +70,7 @@ def run_and_compare(L, U, W, A, k, beam_w, N, reqs=None, mask=True):
     g = out.numpy()
     reqs = list(range(batch)) if reqs is None else reqs
     o = oracle.build_tree(L[reqs], U, W, A[reqs], k, beam_w, N)
-    bins = {"exact": 0, "near": 0}
-    worst = 0.0
-    for j, q in enumerate(reqs):
-        gq = {k2: g[k2][[q]] for k2 in ("tok", "parent", "depth", "score",
-                                         "n_nodes")}
-        oq = {k2: o[k2][[j]] for k2 in o}
-        res, det = compare_trees(gq, oq, 0, N)
-        assert res != "fail", (q, det)
-        bins[res] += 1
-        if res == "exact":
-            worst = max(worst, det)
-        else:
-            _valid_near_tie(gq, 0, L[[q]], U, W, A[[q]], B)
-        if mask:
-            want = oracle.mask(g["parent"][q], int(g["n_nodes"][q]), N)
-            assert np.array_equal(g["mask"][q], want), q
-    print(f"bins {bins}, max |dscore| {worst:.2e}")
+    bins = compare_all(g, o, L, U, W, A, k, beam_w, N, reqs, mask)
     return g, o, bins
 
 
@@ -168,49 +168,118 @@ def test_b7_workload_full():
     run_and_compare(L, U, W, A, w.k, w.beam_w, w.N)
 
 
-def test_b16_workload_sampled():
-    # the benchmark's workload at full size; two requests go through the
-    # oracle (seconds each), the rest through the structural checks
+def test_b16_workload_full():
+    # the benchmark's workload at full size, every request against the
+    # oracle's trees (golden file), the masks against their definition
     w = synth.TREE_WORKLOADS["b16"]
+    o = _golden("b16")
     L, U, W, A = synth.tree_inputs(w)
-    g, o, bins = run_and_compare(L, U, W, A, w.k, w.beam_w, w.N,
-                                 reqs=[0, 31])
-    for q in range(w.batch):
-        n = int(g["n_nodes"][q])
-        assert n == w.N
-        check_structure(g["tok"][q], g["parent"][q], g["depth"][q], n, w.B)
-        sc = g["score"][q]
-        assert np.all(sc[:-1] >= sc[1:])
+    dU, dW = dev_factors(U, W)
+    announce("build b16", dict(batch=w.batch, N=w.N))
+    tb = pct.TreeBuilder(w.batch, w.B, w.V, w.k, w.beam_w, w.N, r=w.r,
+                         bf16=True, mask=True)
+    g = tb.run(dev_f32(L), dU, dW, dev_i32(A)).numpy()
+    torch.cuda.synchronize()
+    bins = compare_all(g, o, L, U, W, A, w.k, w.beam_w, w.N,
+                       list(range(w.batch)))
+    assert bins["exact"] + bins["near"] == w.batch
+    assert bins["near"] <= w.batch // 16, bins
 
 
-def test_round_workload_sampled():
+def test_round_workload_full():
     # the full round at its own size (batch 128, N = 512, 512x512 masks,
-    # acceptance walk): three requests through the oracle, every tree
-    # through the structural checks, every walk against the oracle's walk
+    # acceptance walk): every tree against the oracle's (golden file), every
+    # mask against its definition, every walk against the oracle's walk
     w = synth.TREE_WORKLOADS["round"]
+    o = _golden("round")
     print("generating the round inputs (1.2 GB of logits)", flush=True)
     L, U, W, A = synth.tree_inputs(w)
-    g, o, bins = run_and_compare(L, U, W, A, w.k, w.beam_w, w.N,
-                                 reqs=[0, 77, 127])
-    for q in range(w.batch):
-        n = int(g["n_nodes"][q])
-        assert n == w.N
-        check_structure(g["tok"][q], g["parent"][q], g["depth"][q], n, w.B)
-        sc = g["score"][q]
-        assert np.all(sc[:-1] >= sc[1:])
+    dU, dW = dev_factors(U, W)
+    announce("build round", dict(batch=w.batch, N=w.N))
+    tb = pct.TreeBuilder(w.batch, w.B, w.V, w.k, w.beam_w, w.N, r=w.r,
+                         bf16=True, mask=True)
+    g = tb.run(dev_f32(L), dU, dW, dev_i32(A)).numpy()
+    torch.cuda.synchronize()
+    bins = compare_all(g, o, L, U, W, A, w.k, w.beam_w, w.N,
+                       list(range(w.batch)))
+    assert bins["exact"] + bins["near"] == w.batch
+    assert bins["near"] <= w.batch // 16, bins
     tgt = synth.targets_from_tree(w.seed, g["tok"], g["parent"], g["depth"],
                                   g["n_nodes"], A, w.V, w.B,
                                   synth.round_agreement(w.B))
     announce("round verify", dict(batch=w.batch, N=w.N))
-    tau, an, at = pct.verify_accept(dev_i32(g["tok"]), dev_i32(g["parent"]),
-                                    dev_i32(g["depth"]), dev_i32(g["n_nodes"]),
-                                    dev_i32(tgt), w.B)
-    tau, an, at = tau.cpu().numpy(), an.cpu().numpy(), at.cpu().numpy()
-    for q in range(w.batch):
-        t2, an2, at2 = oracle.accept(g["tok"][q], g["parent"][q],
-                                     int(g["n_nodes"][q]), w.B, tgt[q])
-        assert tau[q] == t2 and list(an[q]) == list(an2) and \
-            list(at[q]) == list(at2), q
+    args = (dev_i32(g["tok"]), dev_i32(g["parent"]), dev_i32(g["depth"]),
+            dev_i32(g["n_nodes"]), dev_i32(tgt), w.B)
+    walks = [pct.verify_accept(*args),
+             pct.verify_accept(*args, mask=tb.out.mask)]
+    for tau, an, at in walks:
+        tau, an, at = tau.cpu().numpy(), an.cpu().numpy(), at.cpu().numpy()
+        for q in range(w.batch):
+            t2, an2, at2 = oracle.accept(g["tok"][q], g["parent"][q],
+                                         int(g["n_nodes"][q]), w.B, tgt[q])
+            assert tau[q] == t2 and list(an[q]) == list(an2) and \
+                list(at[q]) == list(at2), q
+    print(f"round: mean tau {tau.mean():.3f}")
+
+
+@pytest.mark.parametrize("case", ["pool_below_N", "k48_seedless",
+                                  "fp32_factors", "bf16_rank48"])
+def test_other_build_paths(case):
+    # paths of pct_build_tree outside the MFMA fast path: a pool smaller
+    # than the budget (padded outputs), k above the 32 seed tokens (no seed
+    # thresholds), fp32 factors and a bf16 rank that is not a multiple of
+    # 32 (the plain VALU kernel)
+    if case == "pool_below_N":
+        L, U, W, A = _random(31, 3, 3, 3000, 256)
+        k, beam, N = 4, 2, 40   # pool 4 + 8 + 8 = 20 < 40
+    elif case == "k48_seedless":
+        L, U, W, A = _random(32, 4, 3, 6000, 128)
+        k, beam, N = 48, 8, 150
+    elif case == "fp32_factors":
+        L, U, W, A = _random(33, 3, 4, 2500, 48, bf16=False)
+        k, beam, N = 8, 12, 60
+    else:
+        L, U, W, A = _random(34, 3, 4, 2500, 48)
+        k, beam, N = 8, 12, 60
+    g, o, bins = run_and_compare(L, U, W, A, k, beam, N)
+    if case == "pool_below_N":
+        for q in range(L.shape[0]):
+            n = int(g["n_nodes"][q])
+            assert n == 20
+            assert np.all(g["tok"][q][n:] == -1)
+            assert np.all(g["parent"][q][n:] == -1)
+            assert np.all(g["depth"][q][n:] == 0)
+            assert np.all(np.isneginf(g["score"][q][n:]))
+
+
+def _near_one_hot(seed, batch, B, V):
+    """Rows of log-probabilities with a top-1 probability above 1 - 1e-7:
+    the row maximum is within 1e-7 of 0 and every other entry is tiny."""
+    rng = np.random.default_rng(seed)
+    rest = rng.normal(size=(batch, B, V)) - 24.0
+    top = rng.integers(0, V, size=(batch, B))
+    for q in range(batch):
+        for d in range(B):
+            rest[q, d, top[q, d]] = 0.0
+    m = rest.max(axis=2, keepdims=True)
+    lse = m + np.log(np.exp(rest - m).sum(axis=2, keepdims=True))
+    return (rest - lse).astype(np.float32)
+
+
+def test_near_one_hot_rows_keep_children_below_parents():
+    # z - lse is never positive, so a child never outscores its parent and
+    # parents always precede children in the output
+    L = _near_one_hot(41, 4, 5, 3000)
+    A = np.arange(4, dtype=np.int32)
+    g, o, bins = run_and_compare(L, None, None, A, 4, 8, 60)
+    for q in range(4):
+        n = int(g["n_nodes"][q])
+        assert np.all(g["score"][q][:n] <= 0.0)
+        for i in range(n):
+            p = int(g["parent"][q][i])
+            assert p < i
+    U, W = synth.markov_factors(41, 3000, 32, True)
+    g, o, bins = run_and_compare(L, U, W, A, 4, 8, 60)
 
 
 def test_verify_standalone_matches_oracle():
@@ -223,19 +292,23 @@ def test_verify_standalone_matches_oracle():
     tgt = synth.targets_from_tree(21, o["tok"], o["parent"], o["depth"],
                                   o["n_nodes"], A, V, B, lambda d: 0.7)
     announce("verify standalone")
-    tau, an, at = pct.verify_accept(dev_i32(o["tok"]), dev_i32(o["parent"]),
-                                    dev_i32(o["depth"]), dev_i32(o["n_nodes"]),
-                                    dev_i32(tgt), B)
-    tau, an, at = tau.cpu().numpy(), an.cpu().numpy(), at.cpu().numpy()
-    for q in range(batch):
-        t2, an2, at2 = oracle.accept(o["tok"][q], o["parent"][q],
-                                     int(o["n_nodes"][q]), B, tgt[q])
-        assert tau[q] == t2 and list(an[q]) == list(an2) and \
-            list(at[q]) == list(at2), q
-        t3, an3, at3 = naive_accept(o["tok"][q], o["parent"][q],
-                                    o["depth"][q], int(o["n_nodes"][q]),
-                                    tgt[q], B)
-        assert t3 == t2
+    masks = np.stack([oracle.mask(o["parent"][q], int(o["n_nodes"][q]), N)
+                      for q in range(batch)])
+    dmask = torch.from_numpy(masks.view(np.int64)).cuda()
+    args = (dev_i32(o["tok"]), dev_i32(o["parent"]), dev_i32(o["depth"]),
+            dev_i32(o["n_nodes"]), dev_i32(tgt), B)
+    for mk in (None, dmask):
+        tau, an, at = pct.verify_accept(*args, mask=mk)
+        tau, an, at = tau.cpu().numpy(), an.cpu().numpy(), at.cpu().numpy()
+        for q in range(batch):
+            t2, an2, at2 = oracle.accept(o["tok"][q], o["parent"][q],
+                                         int(o["n_nodes"][q]), B, tgt[q])
+            assert tau[q] == t2 and list(an[q]) == list(an2) and \
+                list(at[q]) == list(at2), q
+            t3, an3, at3 = naive_accept(o["tok"][q], o["parent"][q],
+                                        o["depth"][q], int(o["n_nodes"][q]),
+                                        tgt[q], B)
+            assert t3 == t2
 
 
 def test_verify_worked_example():

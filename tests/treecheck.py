@@ -107,24 +107,3 @@ def closed_subsets(prefixes, n):
         chosen = {pset[i] for i in combo}
         if all(len(p) == 1 or p[:-1] in chosen for p in chosen):
             yield combo
-
-
-def compare_trees(g, o, q, N):
-    """Compare GPU result g and oracle result o for request q.
-    Returns ('exact'|'near'|'fail', detail)."""
-    n_o = int(o["n_nodes"][q])
-    n_g = int(g["n_nodes"][q])
-    same = (n_o == n_g and
-            np.array_equal(g["tok"][q], o["tok"][q]) and
-            np.array_equal(g["parent"][q], o["parent"][q]) and
-            np.array_equal(g["depth"][q], o["depth"][q]))
-    if same:
-        d = np.abs(g["score"][q][:n_o].astype(np.float64)
-                   - o["score"][q][:n_o].astype(np.float64))
-        md = float(d.max()) if n_o else 0.0
-        if md <= SCORE_TOL:
-            return "exact", md
-        return "fail", f"score diff {md}"
-    if float(o["min_gap"][q]) < NEAR_TIE:
-        return "near", float(o["min_gap"][q])
-    return "fail", "topology differs without a near tie"
