@@ -73,6 +73,13 @@ def lib():
             P, P, P, sz, P]
         L.pct_build_tree_adaptive_workspace.argtypes = [i32, i32, i32, i32]
         L.pct_build_tree_adaptive_workspace.restype = sz
+    L.pct_build_tree_adaptive_pc.argtypes = [
+        C.POINTER(TreeShape), P, P, P, P, P, C.POINTER(CostModel), P, P, P, P,
+        P, P, P, P, P, sz, P]
+    L.pct_build_tree_adaptive_pc_workspace.argtypes = [C.POINTER(TreeShape)]
+    L.pct_build_tree_adaptive_pc_workspace.restype = sz
+    L.pct_throughput_curve.argtypes = [i32, i32, P, P, P,
+                                       C.POINTER(CostModel), P, P]
     L.pct_profile_enable.argtypes = [i32]
     L.pct_profile_reset.argtypes = []
     L.pct_profile_read.argtypes = [i32, i64, C.POINTER(C.c_double),
@@ -88,13 +95,16 @@ def exported_symbols():
     return ["pct_markov_logits", "pct_markov_logits_workspace",
             "pct_build_tree", "pct_build_tree_workspace",
             "pct_build_tree_adaptive", "pct_build_tree_adaptive_workspace",
+            "pct_build_tree_adaptive_pc",
+            "pct_build_tree_adaptive_pc_workspace", "pct_throughput_curve",
             "pct_tree_mask", "pct_verify_accept", "pct_profile_enable",
             "pct_profile_reset", "pct_profile_read", "pct_status_string",
             "pct_last_error"]
 
 
 PROF_MARKOV, PROF_EXPAND, PROF_TOPN, PROF_MASK, PROF_ACCEPT, PROF_ROWTOP, \
-    PROF_INIT, PROF_ROWSTATS, PROF_BESTFIRST, PROF_FINALIZE = range(10)
+    PROF_INIT, PROF_ROWSTATS, PROF_BESTFIRST, PROF_FINALIZE, PROF_STOP = \
+    range(11)
 
 
 def profile_enable(on: bool = True):
@@ -307,6 +317,87 @@ def build_tree_adaptive(L, ctx_len, n_max: int, cost: dict | None,
     ab = AdaptiveBuilder(batch, B, V, n_max, cost, mask=mask,
                          device=_dev(L))
     return ab.run(L.contiguous(), ctx_len.to(torch.int32).contiguous())
+
+
+# ---------------------------------------------------------------------------
+# pct_build_tree_adaptive_pc / pct_throughput_curve
+
+def _cost_struct(cost):
+    return None if cost is None else CostModel(
+        cost["C_d"], cost["c0"], cost["c1"], cost["c2"], cost["c_ell"])
+
+
+class AdaptivePCBuilder:
+    """Throughput stop on the parent-conditioned tree, fixed shape (N is
+    the largest tree considered)."""
+
+    def __init__(self, batch: int, B: int, V: int, k: int, beam_w: int,
+                 n_max: int, cost: dict | None, r: int = 0,
+                 bf16: bool = True, mask: bool = False, device="cuda"):
+        self.shape = TreeShape(batch, B, V, r, k, beam_w, n_max,
+                               PCT_BF16 if bf16 else PCT_F32)
+        self.cost = _cost_struct(cost)
+        self.device = torch.device(device)
+        nbytes = lib().pct_build_tree_adaptive_pc_workspace(
+            C.byref(self.shape))
+        if nbytes == 0:
+            raise PCTError(1, lib().pct_last_error().decode())
+        self.ws = _workspace(nbytes, self.device)
+        dev = self.device
+        words = (n_max + 63) // 64
+        self.tok = torch.empty(batch, n_max, dtype=torch.int32, device=dev)
+        self.parent = torch.empty_like(self.tok)
+        self.depth = torch.empty_like(self.tok)
+        self.score = torch.empty(batch, n_max, dtype=torch.float32, device=dev)
+        self.n_star = torch.empty(batch, dtype=torch.int32, device=dev)
+        self.phi = torch.empty(batch, dtype=torch.float64, device=dev)
+        self.throughput = torch.empty(batch, dtype=torch.float64, device=dev)
+        self.mask = (torch.empty(batch, n_max, words, dtype=torch.int64,
+                                 device=dev) if mask else None)
+
+    def run(self, L, U, W, anchor, ctx_len):
+        _check(lib().pct_build_tree_adaptive_pc(
+            C.byref(self.shape), _ptr(L), _ptr(U), _ptr(W), _ptr(anchor),
+            _ptr(ctx_len), None if self.cost is None else C.byref(self.cost),
+            _ptr(self.tok), _ptr(self.parent), _ptr(self.depth),
+            _ptr(self.score), _ptr(self.n_star), _ptr(self.phi),
+            _ptr(self.throughput), _ptr(self.mask), _ptr(self.ws),
+            self.ws.numel(), _stream(self.device)))
+        return self
+
+    def numpy(self):
+        out = {k: getattr(self, k).cpu().numpy()
+               for k in ("tok", "parent", "depth", "score", "n_star", "phi",
+                         "throughput")}
+        if self.mask is not None:
+            out["mask"] = self.mask.cpu().numpy().view("uint64")
+        return out
+
+
+def build_tree_adaptive_pc(L, U, W, anchor, ctx_len, k: int, beam_w: int,
+                           n_max: int, cost: dict | None,
+                           mask: bool = False) -> AdaptivePCBuilder:
+    dev = _dev(L)
+    batch, B, V = (int(x) for x in L.shape)
+    U, W, dt, r = _factors(U, W)
+    ab = AdaptivePCBuilder(batch, B, V, k, beam_w, n_max, cost, r=r,
+                           bf16=(dt == PCT_BF16), mask=mask, device=dev)
+    return ab.run(L.contiguous(), U, W, anchor.to(torch.int32).contiguous(),
+                  ctx_len.to(torch.int32).contiguous())
+
+
+def throughput_curve(score, n_nodes, ctx_len, cost: dict | None):
+    """f(n) = (1 + Phi_n) / D(n) for n = 0..N of best-first-ordered scores
+    [batch][N]; returns [batch][N+1] float64."""
+    dev = _dev(score)
+    batch, N = (int(x) for x in score.shape)
+    f = torch.empty(batch, N + 1, dtype=torch.float64, device=dev)
+    cm = _cost_struct(cost)
+    _check(lib().pct_throughput_curve(
+        batch, N, _ptr(score.contiguous()), _ptr(n_nodes.contiguous()),
+        _ptr(None if ctx_len is None else ctx_len.contiguous()),
+        None if cm is None else C.byref(cm), _ptr(f), _stream(dev)))
+    return f
 
 
 # ---------------------------------------------------------------------------

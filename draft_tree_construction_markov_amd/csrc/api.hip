@@ -462,6 +462,37 @@ pct_status pct_build_tree(const pct_tree_shape* shape, const float* L,
 
 // ------------------------------------------------------------------------
 namespace {
+pct_status check_cost(const pct_cost_model* cost) {
+  if (!cost) return PCT_OK;
+  if (!(cost->c1 >= 0.0) || !(cost->c2 >= 0.0) || !(cost->c_ell >= 0.0))
+    return fail(PCT_ERR_INVALID_ARG,
+                "cost model must be convex and increasing (c1, c2, c_ell "
+                ">= 0)");
+  if (!(cost->C_d + cost->c0 > 0.0))
+    return fail(PCT_ERR_INVALID_ARG, "round cost at n = 0 must be > 0");
+  return PCT_OK;
+}
+
+StopArgs stop_args(int N, const int32_t* n_avail, const float* score,
+                   const int32_t* ctx_len, const pct_cost_model* cost) {
+  StopArgs a{};
+  a.N = N;
+  a.n_avail = n_avail;
+  a.score = score;
+  a.ctx_len = cost ? ctx_len : nullptr;
+  a.has_cost = cost != nullptr;
+  if (cost) {
+    a.C_d = cost->C_d;
+    a.c0 = cost->c0;
+    a.c1 = cost->c1;
+    a.c2 = cost->c2;
+    a.c_ell = cost->c_ell;
+  }
+  return a;
+}
+}  // namespace
+
+namespace {
 struct AdaptiveWs {
   float* lse_f;
   int32_t* ltok_f;
@@ -531,14 +562,8 @@ pct_status pct_build_tree_adaptive(int32_t batch, int32_t B, int32_t V,
   if (!L || !tok || !parent || !depth || !score || !n_star || !phi ||
       !throughput || !workspace || (cost && !ctx_len))
     return fail(PCT_ERR_INVALID_ARG, "required pointer is NULL");
-  if (cost) {
-    if (!(cost->c1 >= 0.0) || !(cost->c2 >= 0.0) || !(cost->c_ell >= 0.0))
-      return fail(PCT_ERR_INVALID_ARG,
-                  "cost model must be convex and increasing (c1, c2, c_ell "
-                  ">= 0)");
-    if (!(cost->C_d + cost->c0 > 0.0))
-      return fail(PCT_ERR_INVALID_ARG, "round cost at n = 0 must be > 0");
-  }
+  st = check_cost(cost);
+  if (st != PCT_OK) return st;
   AdaptiveWs w;
   int Kf, Ks;
   const size_t need = carve_adaptive(batch, B, V, n_max, nullptr, w, Kf, Ks);
@@ -596,6 +621,74 @@ pct_status pct_build_tree_adaptive(int32_t batch, int32_t B, int32_t V,
     e = launch_mask(batch, n_max, parent, n_star, mask, s);
     if (e != hipSuccess) return hip_fail(e, "mask kernel");
   }
+  return PCT_OK;
+}
+
+// ------------------------------------------------------------------------
+
+size_t pct_build_tree_adaptive_pc_workspace(const pct_tree_shape* shape) {
+  return pct_build_tree_workspace(shape);
+}
+
+pct_status pct_build_tree_adaptive_pc(
+    const pct_tree_shape* shape, const float* L, const void* U,
+    const void* W, const int32_t* anchor, const int32_t* ctx_len,
+    const pct_cost_model* cost, int32_t* tok, int32_t* parent,
+    int32_t* depth, float* score, int32_t* n_star, double* phi,
+    double* throughput, uint64_t* mask, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  pct_status st = check_cost(cost);
+  if (st != PCT_OK) return st;
+  if (!n_star || !phi || !throughput || (cost && !ctx_len))
+    return fail(PCT_ERR_INVALID_ARG, "required pointer is NULL");
+  // the tree in key order (a best-first order of its nodes); n_star holds
+  // the node counts until the stop overwrites it
+  st = pct_build_tree(shape, L, U, W, anchor, tok, parent, depth, score,
+                      n_star, nullptr, workspace, workspace_bytes, stream);
+  if (st != PCT_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  StopArgs a = stop_args(shape->N, n_star, score, ctx_len, cost);
+  a.n_star = n_star;
+  a.phi = phi;
+  a.thr = throughput;
+  a.tok = tok;
+  a.parent = parent;
+  a.depth = depth;
+  a.score_out = score;
+  hipError_t e;
+  {
+    ProfScope ps(PROF_STOP, shape->batch, s);
+    e = launch_stop_scan(shape->batch, a, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "stop kernel");
+  if (mask) {
+    ProfScope ps(PROF_MASK, shape->batch, s);
+    e = launch_mask(shape->batch, shape->N, parent, n_star, mask, s);
+    if (e != hipSuccess) return hip_fail(e, "mask kernel");
+  }
+  return PCT_OK;
+}
+
+pct_status pct_throughput_curve(int32_t batch, int32_t N, const float* score,
+                                const int32_t* n_nodes,
+                                const int32_t* ctx_len,
+                                const pct_cost_model* cost, double* f,
+                                void* stream) {
+  if (batch < 1 || N < 1)
+    return fail(PCT_ERR_INVALID_ARG, "need batch, N >= 1");
+  if (!score || !n_nodes || !f || (cost && !ctx_len))
+    return fail(PCT_ERR_INVALID_ARG, "required pointer is NULL");
+  pct_status st = check_cost(cost);
+  if (st != PCT_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  StopArgs a = stop_args(N, n_nodes, score, ctx_len, cost);
+  a.f = f;
+  hipError_t e;
+  {
+    ProfScope ps(PROF_STOP, batch, s);
+    e = launch_stop_scan(batch, a, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "throughput curve kernel");
   return PCT_OK;
 }
 

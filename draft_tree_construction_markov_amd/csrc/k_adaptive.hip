@@ -790,3 +790,96 @@ hipError_t launch_bestfirst(int batch, int B, int V, int n_max, int klist,
 }
 
 }  // namespace pct
+
+namespace pct {
+
+// ---------------------------------------------------------------------
+// Throughput stop over an ordered tree (CaDDTree summary, "Method": the
+// tree of the first n nodes of a best-first order has throughput
+// f(n) = (1 + Phi_n) / D(n); nodes are added while the gain
+// g(n) = P_{n+1} D(n) - (1 + Phi_n)(D(n+1) - D(n)) is positive).
+// One wave per request.  Every n is tested at once: each lane takes a
+// contiguous chunk of the list, the chunk sums of P_i = exp(s_i) are
+// prefix-summed across the wave (double), each lane then walks its chunk
+// with the exact Phi_n, and n* is the wave minimum of the lanes' first
+// non-positive gains.
+
+__device__ __forceinline__ double shfl_up_d(double x, int delta) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const int lo = __shfl_up((int)(uint32_t)u, delta, kWave);
+  const int hi = __shfl_up((int)(uint32_t)(u >> 32), delta, kWave);
+  return __builtin_bit_cast(double,
+                            ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+__global__ __launch_bounds__(64) void stop_scan_kernel(StopArgs a) {
+  const int q = blockIdx.x, lane = threadIdx.x;
+  const float* sc = a.score + (int64_t)q * a.N;
+  // n_star may alias n_avail: read it before anything is written
+  const int n = min(max(a.n_avail[q], 0), a.N);
+  __builtin_amdgcn_wave_barrier();
+  const double ell = a.ctx_len ? (double)a.ctx_len[q] : 0.0;
+  auto D = [&](double m) {
+    return a.has_cost ? a.C_d + a.c0 + a.c1 * m + a.c2 * m * m +
+                            a.c_ell * ell * m
+                      : 1.0;
+  };
+  const int per = (n + kWave - 1) / kWave;
+  const int b0 = min(lane * per, n), b1 = min(b0 + per, n);
+  double loc = 0.0;
+  for (int i = b0; i < b1; ++i) loc += exp((double)sc[i]);
+  // inclusive prefix over the lanes
+  double inc = loc;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const double o = shfl_up_d(inc, d);
+    if (lane >= d) inc += o;
+  }
+  double Phi = inc - loc;  // Phi at the chunk start
+  int first = n;
+  double* f = a.f ? a.f + (int64_t)q * (a.N + 1) : nullptr;
+  for (int i = b0; i < b1; ++i) {
+    const double P = exp((double)sc[i]);
+    if (a.has_cost && first == n) {
+      const double Di = D((double)i);
+      const double g = P * Di - (1.0 + Phi) * (D((double)i + 1.0) - Di);
+      if (g <= 0.0) first = i;
+    }
+    if (f) f[i] = (1.0 + Phi) / D((double)i);
+    Phi += P;
+  }
+  const int ns = a.has_cost ? -wave_max(-first) : n;
+  if (f) {
+    // the whole list's throughput, repeated past it (a budget above the
+    // available nodes builds the same tree)
+    const double total = wave_max(lane == kWave - 1 ? inc : -1.0);
+    const double fn = (1.0 + total) / D((double)n);
+    for (int i = n + lane; i <= a.N; i += kWave) f[i] = fn;
+  }
+  // Phi(n*) in the same chunked order
+  double ps = 0.0;
+  for (int i = b0; i < min(b1, ns); ++i) ps += exp((double)sc[i]);
+  const double phi = wave_sum(ps);
+  if (lane == 0) {
+    if (a.n_star) a.n_star[q] = ns;
+    if (a.phi) a.phi[q] = phi;
+    if (a.thr) a.thr[q] = (1.0 + phi) / D((double)ns);
+  }
+  if (a.tok) {
+    __builtin_amdgcn_wave_barrier();
+    for (int i = ns + lane; i < a.N; i += kWave) {
+      const int64_t o = (int64_t)q * a.N + i;
+      a.tok[o] = -1;
+      a.parent[o] = -1;
+      a.depth[o] = 0;
+      a.score_out[o] = neg_inf();
+    }
+  }
+}
+
+hipError_t launch_stop_scan(int batch, const StopArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(stop_scan_kernel, dim3(batch), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace pct

@@ -90,7 +90,8 @@ enum ProfKind {
   PROF_INIT = 6,     // depth-1 frontier
   PROF_ROWSTATS = 7, // adaptive: streaming log-softmax + select
   PROF_BESTFIRST = 8,// adaptive: best-first order + stop
-  PROF_FINALIZE = 9  // standalone Markov call: per-parent results
+  PROF_FINALIZE = 9, // standalone Markov call: per-parent results
+  PROF_STOP = 10     // throughput stop / curve scan
 };
 
 // RAII bracket of one launch (no-op unless profiling is enabled).
@@ -194,6 +195,25 @@ hipError_t launch_rowpart(const float* L, int rows, int V, int K, int kstride,
                           float* lse, int32_t* ltok, float* llp,
                           hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
+
+// Throughput stop / curve over best-first-ordered trees (one wave per
+// request).  Pointers that are null are not written.
+struct StopArgs {
+  int N;                   // row stride of the ordered lists
+  const int32_t* n_avail;  // [batch] nodes in each list (may alias n_star)
+  const float* score;      // [batch][N] scores in best-first order
+  const int32_t* ctx_len;  // [batch] or null (no cost model)
+  int has_cost;
+  double C_d, c0, c1, c2, c_ell;
+  int32_t* n_star;  // [batch]
+  double* phi;      // [batch] Phi(n*)
+  double* thr;      // [batch] (1 + Phi(n*)) / D(n*)
+  double* f;        // [batch][N+1] f(n) = (1 + Phi_n) / D(n)
+  // pads written past n* (tok -1, parent -1, depth 0, score -inf)
+  int32_t *tok, *parent, *depth;
+  float* score_out;
+};
+hipError_t launch_stop_scan(int batch, const StopArgs& a, hipStream_t s);
 hipError_t launch_mask(int batch, int N, const int32_t* parent,
                        const int32_t* n_nodes, uint64_t* mask, hipStream_t s);
 hipError_t launch_accept(int batch, int N, int B, const int32_t* tok,

@@ -183,6 +183,59 @@ size_t pct_build_tree_adaptive_workspace(int32_t batch, int32_t B, int32_t V,
                                          int32_t n_max);
 
 /* ------------------------------------------------------------------------
+ * pct_build_tree_adaptive_pc -- [CAD] "Method" on the parent-conditioned
+ * tree of [PCT] "straight draft": the throughput stop over the key order of
+ * a pct_build_tree build.  The build (shape, L, U, W, anchor as for
+ * pct_build_tree, with N = n_max, the largest tree considered) yields its
+ * nodes in key order, which is a best-first order: every node comes after
+ * its parent.  With P_i = exp(score_i), Phi_n = sum_{i<=n} P_i and
+ * D(n) = C(n; l), the tree keeps the first n* nodes, n* being the first n
+ * whose gain g(n) = P_{n+1} D(n) - (1 + Phi_n)(D(n+1) - D(n)) is not
+ * positive.  When k >= n* and beam_w >= n*, the kept nodes are the n* most
+ * probable prefixes of the parent-conditioned drafter, i.e. the greedy
+ * best-first tree (a top-n prefix has sibling rank < n and depth rank < n,
+ * so the beam keeps it); with smaller k or beam_w it is the beam's
+ * approximation of it.  cost NULL => n* = the number of nodes built.
+ *
+ *  tok, parent, depth, score  [batch][N] out: the first n_star entries are
+ *           the tree, the rest pads (tok -1, parent -1, depth 0,
+ *           score -inf)
+ *  ctx_len  [batch] context length l of each request (needed with cost)
+ *  n_star   [batch] out; phi [batch] out Phi(n*); throughput [batch] out
+ *           (1 + Phi)/D(n*) (1 + Phi without a cost model)
+ *  mask     [batch][N][ceil(N/64)] out, optional: the kept tree's mask
+ *  workspace  pct_build_tree_adaptive_pc_workspace(shape) bytes
+ * Errors: as pct_build_tree; a cost model with negative c1, c2 or c_ell, or
+ * with C_d + c0 <= 0, is rejected with PCT_ERR_INVALID_ARG. */
+pct_status pct_build_tree_adaptive_pc(
+    const pct_tree_shape* shape /*host*/, const float* L, const void* U,
+    const void* W, const int32_t* anchor, const int32_t* ctx_len,
+    const pct_cost_model* cost /*host*/, int32_t* tok, int32_t* parent,
+    int32_t* depth, float* score, int32_t* n_star, double* phi,
+    double* throughput, uint64_t* mask, void* workspace,
+    size_t workspace_bytes, void* stream);
+size_t pct_build_tree_adaptive_pc_workspace(const pct_tree_shape* shape /*host*/);
+
+/* ------------------------------------------------------------------------
+ * pct_throughput_curve -- [CAD] "Method": the throughput of every prefix
+ * of a best-first-ordered tree, f(n) = (1 + Phi_n) / D(n) for n = 0..N
+ * (D = 1 without a cost model), as a fixed-budget (DDTree-style) build of n
+ * nodes would get it; the oracle budget of a round is the n that maximises
+ * it.  Budgets above a request's n_nodes repeat f(n_nodes).
+ *  score    [batch][N] scores in best-first order (e.g. the output of a
+ *           build without a cost model), n_nodes [batch]
+ *  ctx_len  [batch] (needed with cost)
+ *  f        [batch][N+1] out
+ * Needs no workspace.
+ * Errors: PCT_ERR_INVALID_ARG for batch < 1, N < 1, null required pointers
+ * or a cost model that is not convex and increasing. */
+pct_status pct_throughput_curve(int32_t batch, int32_t N, const float* score,
+                                const int32_t* n_nodes,
+                                const int32_t* ctx_len,
+                                const pct_cost_model* cost /*host*/,
+                                double* f, void* stream);
+
+/* ------------------------------------------------------------------------
  * pct_tree_mask -- [PCT] "straight draft": the whole tree is verified in one
  * target forward, in which a node may see only itself and its ancestors.
  *  parent  [batch][N] (-1 = root), n_nodes [batch]
@@ -229,7 +282,7 @@ pct_status pct_verify_accept(int32_t batch, int32_t N, int32_t B,
  * (units = parents of the launch), 1 per-request expand, 2 global top-N,
  * 3 mask, 4 acceptance walk, 5 seed pre-pass (units = rows), 6 depth-1
  * init, 7 adaptive row statistics (units = rows), 8 adaptive best-first +
- * stop, 9 standalone per-parent results.
+ * stop, 9 standalone per-parent results, 10 throughput stop / curve scan.
  *  pct_profile_enable  turns recording on or off (the event pool, 8192
  *                      launches, is created on the first enable)
  *  pct_profile_reset   forgets recorded launches

@@ -243,6 +243,17 @@ def adaptive_round(seed: int, batch: int, B: int, V: int, var: float = 3.0,
     return L, peaked, ctx.astype(np.int32)
 
 
+def context_lengths(seed: int, batch: int, lo: int = 512, hi: int = 32768,
+                    req0: int = 0) -> np.ndarray:
+    """Context length per request, log-uniform over [lo, hi] (the same draw
+    as adaptive_round's)."""
+    reqs = np.arange(req0, req0 + batch, dtype=np.uint64)
+    ctxu = uniform(seed, TAG_CTX, reqs)
+    return np.rint(np.exp(math.log(lo) + ctxu * (math.log(hi) -
+                                                 math.log(lo)))).astype(
+        np.int32)
+
+
 # --------------------------------------------------------------------------
 # synthetic target tokens for the acceptance walk
 

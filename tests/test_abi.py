@@ -135,3 +135,26 @@ def test_build_tree_rejects_unaligned_factors():
                                 d, need, None)
         assert rc == 1
         assert b"aligned" in lib.pct_last_error()
+
+
+def test_adaptive_pc_and_curve_reject_bad_arguments():
+    lib = pct.lib()
+    d = C.c_void_p(256)
+    sh = _shape(r=32, uw_dtype=1, N=16)
+    need = lib.pct_build_tree_adaptive_pc_workspace(C.byref(sh))
+    assert need == lib.pct_build_tree_workspace(C.byref(sh)) > 0
+    bad = pct.CostModel(1.0, 2.0, -0.004, 0.0, 1e-5)
+    rc = lib.pct_build_tree_adaptive_pc(C.byref(sh), d, d, d, d, d,
+                                        C.byref(bad), d, d, d, d, d, d, d,
+                                        None, d, need, None)
+    assert rc == 1
+    good = pct.CostModel(1.0, 2.0, 0.004, 0.0, 1e-5)
+    # ctx_len is required with a cost model
+    rc = lib.pct_build_tree_adaptive_pc(C.byref(sh), d, d, d, d, None,
+                                        C.byref(good), d, d, d, d, d, d, d,
+                                        None, d, need, None)
+    assert rc == 1
+    assert lib.pct_throughput_curve(0, 4, d, d, d, None, d, None) == 1
+    assert lib.pct_throughput_curve(1, 4, d, None, d, None, d, None) == 1
+    assert lib.pct_throughput_curve(1, 4, d, d, d, C.byref(bad), d,
+                                    None) == 1

@@ -1,0 +1,192 @@
+"""GPU parity of the throughput stop on the parent-conditioned tree
+(pct_build_tree_adaptive_pc) and of the throughput curve
+(pct_throughput_curve) against the CPU oracle:
+
+- the stop over a beam tree's key order equals the oracle's beam tree
+  stopped by the oracle's rule, request by request;
+- with k = beam = N >= n* the kept tree is the greedy best-first tree over
+  the parent-conditioned rows (the oracle's heap-based build);
+- the curve f(n) matches the oracle's, and on the adaptive workload the
+  adaptive budget n* of every round is that round's best fixed budget, so
+  it matches or beats every fixed budget of a grid search on average."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import draft_tree_construction_markov_amd as pct
+import oracle
+import synth
+from gpu_util import announce, dev_f32, dev_factors, dev_i32
+from treecheck import NEAR_TIE, SCORE_TOL, check_structure, path_tokens
+
+pytestmark = pytest.mark.gpu
+
+COST = {k: synth.ADAPTIVE[k] for k in ("C_d", "c0", "c1", "c2", "c_ell")}
+
+
+def _run(L, U, W, A, ctx, k, beam, n_max, cost, label):
+    batch, B, V = L.shape
+    dU, dW = dev_factors(U, W)
+    announce("adaptive-pc", label, dict(batch=batch, B=B, V=V, k=k,
+                                        beam=beam, n_max=n_max))
+    ab = pct.build_tree_adaptive_pc(dev_f32(L), dU, dW, dev_i32(A),
+                                    dev_i32(ctx), k, beam, n_max, cost,
+                                    mask=True)
+    torch.cuda.synchronize()
+    return ab.numpy()
+
+
+def _check_against_beam_oracle(g, L, U, W, A, ctx, k, beam, n_max, cost,
+                               reqs=None):
+    batch, B, V = L.shape
+    reqs = range(batch) if reqs is None else reqs
+    bins = {"exact": 0, "near": 0}
+    for q in reqs:
+        t = oracle.build_tree(L[[q]], U, W, A[[q]], k, beam, n_max)
+        n = int(t["n_nodes"][0])
+        st = oracle.stop(t["score"][0], n, int(ctx[q]), cost)
+        ns = int(g["n_star"][q])
+        same_tree = all(np.array_equal(g[key][q][:ns], t[key][0][:ns])
+                        for key in ("tok", "parent", "depth"))
+        if ns == st["n_star"] and same_tree:
+            d = np.abs(g["score"][q][:ns].astype(np.float64) -
+                       t["score"][0][:ns].astype(np.float64))
+            assert (d.max() if ns else 0.0) <= SCORE_TOL, q
+            assert abs(g["phi"][q] - st["phi"]) <= 1e-4 * max(1.0, st["phi"])
+            assert abs(g["throughput"][q] - st["throughput"]) <= \
+                1e-4 * st["throughput"]
+            bins["exact"] += 1
+        else:
+            # only an oracle near-tie may explain a difference
+            assert t["min_gap"][0] < NEAR_TIE or st["gain_margin"] < 1e-4, \
+                (q, ns, st["n_star"])
+            check_structure(g["tok"][q], g["parent"][q], g["depth"][q], ns, B)
+            bins["near"] += 1
+        assert np.all(g["tok"][q][ns:] == -1)
+        assert np.all(np.isneginf(g["score"][q][ns:]))
+        want = oracle.mask(g["parent"][q], ns, n_max)
+        assert np.array_equal(g["mask"][q], want), q
+    print(f"bins {bins}, n* {[int(x) for x in g['n_star'][:16]]}")
+    return bins
+
+
+def _random(seed, batch, B, V, r, scale=1.7):
+    rng = np.random.default_rng(seed)
+    L = (rng.normal(size=(batch, B, V)) * scale).astype(np.float32)
+    U, W = synth.markov_factors(seed, V, r, True)
+    A = rng.integers(0, V, size=batch).astype(np.int32)
+    ctx = synth.context_lengths(seed, batch)
+    return L, U, W, A, ctx
+
+
+@pytest.mark.parametrize("batch,B,V,r,k,beam,n_max,c1", [
+    (6, 4, 3000, 256, 8, 16, 64, 0.004),
+    (5, 5, 2048, 64, 4, 8, 40, 0.02),
+    (40, 3, 3000, 128, 8, 16, 32, 0.001),   # > 256 parents per launch
+])
+def test_stop_over_the_beam_tree(batch, B, V, r, k, beam, n_max, c1):
+    L, U, W, A, ctx = _random(batch + V, batch, B, V, r)
+    cost = dict(COST, c1=c1)
+    g = _run(L, U, W, A, ctx, k, beam, n_max, cost, "beam")
+    bins = _check_against_beam_oracle(g, L, U, W, A, ctx, k, beam, n_max,
+                                      cost)
+    assert bins["near"] <= max(1, batch // 16)
+    # no cost model: the whole tree
+    g = _run(L, U, W, A, ctx, k, beam, n_max, None, "fixed")
+    _check_against_beam_oracle(g, L, U, W, A, ctx, k, beam, n_max, None)
+
+
+def _check_against_bestfirst(g, L, U, W, A, ctx, n_max, cost, reqs):
+    bins = {"exact": 0, "near": 0}
+    for q in reqs:
+        o = oracle.adaptive(L[q], n_max, int(ctx[q]), cost, U=U, W=W,
+                            anchor=int(A[q]))
+        ns = int(g["n_star"][q])
+        a = {tuple(path_tokens(o["tok"], o["parent"], i))
+             for i in range(o["n_star"])}
+        b = {tuple(path_tokens(g["tok"][q], g["parent"][q], i))
+             for i in range(ns)}
+        if ns == o["n_star"] and a == b:
+            assert abs(g["phi"][q] - o["phi"]) <= 1e-4 * max(1.0, o["phi"])
+            bins["exact"] += 1
+        else:
+            assert o["min_gap"] < NEAR_TIE or o["gain_margin"] < 1e-4, \
+                (q, ns, o["n_star"])
+            bins["near"] += 1
+    print(f"best-first bins {bins}")
+    return bins
+
+
+def test_exact_regime_is_the_best_first_tree():
+    # k = beam = N = n_max: the kept prefixes are the most probable ones
+    L, U, W, A, ctx = _random(77, 8, 4, 2500, 64)
+    for cost in (COST, dict(COST, c0=0.3, c1=0.0005)):
+        g = _run(L, U, W, A, ctx, 24, 24, 24, cost, "exact-regime")
+        bins = _check_against_bestfirst(g, L, U, W, A, ctx, 24, cost,
+                                        range(8))
+        assert bins["near"] <= 1
+
+
+def test_b16_inputs_exact_regime():
+    # the b16 workload's inputs (batch 32, V = 151936, B = 16, rank 256)
+    # with the adaptive workload's cost model and context lengths, in the
+    # exact regime k = beam = N = 20; every request against the oracle's
+    # best-first build over parent-conditioned rows
+    w = synth.TREE_WORKLOADS["b16"]
+    L, U, W, A = synth.tree_inputs(w)
+    ctx = synth.context_lengths(w.seed, w.batch)
+    g = _run(L, U, W, A, ctx, 20, 20, 20, COST, "b16-exact")
+    bins = _check_against_bestfirst(g, L, U, W, A, ctx, 20, COST,
+                                    range(w.batch))
+    assert bins["near"] <= 2
+    print("n*", [int(x) for x in g["n_star"]])
+
+
+def test_throughput_curve_matches_oracle():
+    rng = np.random.default_rng(8)
+    batch, B, V, n_max = 5, 4, 700, 300
+    L = (rng.normal(size=(batch, B, V)) * 2).astype(np.float32)
+    ctx = synth.context_lengths(8, batch)
+    ab = pct.build_tree_adaptive(dev_f32(L), dev_i32(ctx), n_max, None)
+    announce("curve", dict(batch=batch, n_max=n_max))
+    for cost in (COST, None):
+        f = pct.throughput_curve(ab.score, ab.n_star, dev_i32(ctx),
+                                 cost).cpu().numpy()
+        g = ab.numpy()
+        for q in range(batch):
+            want = oracle.throughput_curve(g["score"][q], int(g["n_star"][q]),
+                                           int(ctx[q]), cost)
+            n = int(g["n_star"][q])
+            assert np.allclose(f[q][:n + 1], want, rtol=1e-12, atol=0)
+            assert np.all(f[q][n:] == f[q][n])
+
+
+def test_adaptive_budget_beats_the_best_fixed_budget():
+    # the adaptive workload: fixed-budget trees of every size come from one
+    # build without a cost model (n_max = 1024, best-first order); the
+    # grid search's best fixed budget maximises the mean throughput over
+    # the rounds, the adaptive n* maximises each round's own
+    a = synth.ADAPTIVE
+    L, peaked, ctx = synth.adaptive_round(a["seed"], a["batch"], a["B"],
+                                          a["V"])
+    dL, dC = dev_f32(L), dev_i32(ctx)
+    announce("grid search", dict(batch=a["batch"], n_max=a["n_max"]))
+    fixed = pct.build_tree_adaptive(dL, dC, a["n_max"], None)
+    f = pct.throughput_curve(fixed.score, fixed.n_star, dC,
+                             COST).cpu().numpy()
+    adaptive = pct.build_tree_adaptive(dL, dC, a["n_max"], COST).numpy()
+    ns = adaptive["n_star"]
+    per_round_best = f.max(axis=1)
+    f_adaptive = f[np.arange(a["batch"]), ns]
+    # every round's n* is its own best budget (the curve is unimodal)
+    assert np.allclose(f_adaptive, per_round_best, rtol=1e-9, atol=0)
+    assert np.allclose(adaptive["throughput"], f_adaptive, rtol=1e-9)
+    mean_f = f.mean(axis=0)
+    n_fix = int(np.argmax(mean_f))
+    assert f_adaptive.mean() >= mean_f[n_fix] - 1e-12
+    print(f"best fixed budget {n_fix}: mean f {mean_f[n_fix]:.5f}; "
+          f"adaptive mean f {f_adaptive.mean():.5f} "
+          f"(+{100 * (f_adaptive.mean() / mean_f[n_fix] - 1):.2f}%), "
+          f"n* mean {ns.mean():.2f} std {ns.std():.2f}")
