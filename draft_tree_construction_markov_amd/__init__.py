@@ -97,6 +97,7 @@ def exported_symbols():
             "pct_build_tree_adaptive", "pct_build_tree_adaptive_workspace",
             "pct_build_tree_adaptive_pc",
             "pct_build_tree_adaptive_pc_workspace", "pct_throughput_curve",
+            "pct_build_tree_noalloc",
             "pct_tree_mask", "pct_verify_accept", "pct_profile_enable",
             "pct_profile_reset", "pct_profile_read", "pct_status_string",
             "pct_last_error"]

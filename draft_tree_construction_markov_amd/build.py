@@ -16,7 +16,7 @@ SOURCES = ["api.hip", "k_markov.hip",
            "k_markov_r2s.hip", "k_markov_r2d.hip", "k_markov_r4s.hip",
            "k_markov_r4d.hip", "k_markov_r8s.hip", "k_markov_r8d.hip",
            "k_markov_r16s.hip", "k_markov_r16d.hip", "k_select.hip",
-           "k_verify.hip", "k_adaptive.hip", "profile.hip"]
+           "k_verify.hip", "k_adaptive.hip", "profile.hip", "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

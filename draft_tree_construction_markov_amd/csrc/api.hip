@@ -163,6 +163,13 @@ pct_status check_shape(const pct_tree_shape* sh) {
 
 }  // namespace
 
+namespace pct {
+pct_status set_error(pct_status st, const char* msg) {
+  snprintf(g_err, sizeof g_err, "%s", msg);
+  return st;
+}
+}  // namespace pct
+
 extern "C" {
 
 const char* pct_status_string(pct_status s) {

@@ -105,6 +105,12 @@ class ProfScope {
   int idx_;
 };
 
+// Sets the calling thread's pct_last_error() text and returns st.
+}  // namespace pct
+#include "../../include/pctree.h"
+namespace pct {
+pct_status set_error(pct_status st, const char* msg);
+
 K1Plan plan_k1(int P, int V, int r, int k, int uw_dtype, bool has_uw,
                bool allow_mfma = true, int group_fp = 0);
 hipError_t launch_k1(const K1Plan& pl, const K1Args& a, hipStream_t s);

@@ -275,6 +275,25 @@ pct_status pct_verify_accept(int32_t batch, int32_t N, int32_t B,
                              int32_t* accept_tok, void* stream);
 
 /* ------------------------------------------------------------------------
+ * pct_build_tree_noalloc -- for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): pct_build_tree with the same arguments minus the workspace,
+ * which is instead a fixed 32 MiB device array inside the library, one per
+ * GPU, held until the process ends.  Shapes whose
+ * pct_build_tree_workspace() exceeds 32 MiB return PCT_ERR_UNSUPPORTED
+ * before anything is enqueued (the batch-128, N = 512 round needs about
+ * 21 MB).  Allocates nothing.  All calls on one GPU share its array, so
+ * calls that overlap in time on one GPU (other streams or threads) race;
+ * calls ordered on one stream do not.  Errors otherwise as pct_build_tree. */
+pct_status pct_build_tree_noalloc(const pct_tree_shape* shape /*host*/,
+                                  const float* L, const void* U,
+                                  const void* W, const int32_t* anchor,
+                                  int32_t* tok, int32_t* parent,
+                                  int32_t* depth, float* score,
+                                  int32_t* n_nodes, uint64_t* mask,
+                                  void* stream);
+
+/* ------------------------------------------------------------------------
  * Profiling (not from the pages; for measuring kernels against the
  * hardware roofline).  When enabled, every kernel launch of the calls above
  * is bracketed by two HIP events recorded on its stream, tagged with a kind
