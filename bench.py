@@ -21,10 +21,23 @@ Prints one JSON line (rank 0):
                the fused kernel's launches at depths 1 and 2 (32 and 256
                parents) against HBM peak: W once + the launch's L rows +
                the parents' U rows, per launch
-  cpu_baseline the CPU oracle on a bounded sample of the same workload
+  step_ms      median / p10 / p90 of per-step HIP-event times (a separate
+               pass with one event pair per step)
+  cpu_baseline the CPU oracle on a bounded sample of the same workload, on
+               one pinned host core; cpu_baselines adds the tiny, b7 and
+               adaptive workloads timed in full
+  round        batch 128, N = 512: build, 512x512 masks and the acceptance
+               walk timed separately and summed (medians of per-step events)
+  b7_latency   batch 1, B = 7, N = 64 build + mask latency
   adaptive     the adaptive best-first build (batch 64, n_max 1024) with its
                row-statistics kernels (single-read pieces, their merge and
                the full-length pass) against HBM peak
+  adaptive_pc  the throughput stop on the parent-conditioned tree (the b16
+               inputs, k = beam = N = 20, the adaptive workload's cost model)
+  budget_grid  fixed budgets of every size (one build without a cost model
+               + the throughput curve) against the adaptive budget
+  cost_model   a fit of the verification cost from synthetic latency samples
+               and the throughput lost to fitted or perturbed cost models
 """
 from __future__ import annotations
 
@@ -102,6 +115,8 @@ def parse():
                     help="requests of the workload timed on the CPU oracle")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-adaptive", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="only the b16 workload (profiling runs)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run a plain device copy of this size first "
                          "(traffic-counter calibration)")
@@ -187,6 +202,7 @@ def main():
     torch.cuda.synchronize()
     ms_step_ev = (time.perf_counter() - t3) * 1e3 / args.steps
     pct.profile_enable(False)
+    step_ms = step_stats(torch, step, args.steps)
     P_steady = w.batch * w.beam_w
     k1_ms, k1_n = pct.profile_read(pct.PROF_MARKOV, P_steady)
     k1_all_ms, k1_all_n = pct.profile_read(pct.PROF_MARKOV, -1)
@@ -243,6 +259,7 @@ def main():
                                "mask + acceptance walk",
                    "global_batch": w.batch, "parallelism": "none (1 GPU)"},
         "nodes_per_sec": round(nodes_s, 1),
+        "step_ms": step_ms,
         "ms_per_step_with_events": round(ms_step_ev, 4),
         "kernel_ms_per_step": per_kind,
         "markov_all_launches": {"ms_per_step": round(k1_all_ms / args.steps, 4),
@@ -252,12 +269,181 @@ def main():
         "roofline": roofline,
     }
 
-    if not args.no_adaptive and hasattr(pct.lib(), "pct_build_tree_adaptive"):
-        res["adaptive"] = bench_adaptive(args, pct, synth, torch, dev)
+    if not args.no_extra:
+        res["round"] = bench_round(args, pct, synth, torch, dev)
+        res["b7_latency"] = bench_b7(args, pct, synth, torch, dev)
+        res["adaptive_pc"] = bench_adaptive_pc(args, pct, synth, torch, dev,
+                                               dL, dU, dW, dA)
+    if not args.no_adaptive:
+        res["adaptive"], extra = bench_adaptive(args, pct, synth, torch, dev)
+        if not args.no_extra:
+            res["budget_grid"], res["cost_model"] = extra
 
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(args, w, L, U, W, A)
+        if not args.no_extra:
+            res["cpu_baselines"] = cpu_baselines(synth)
     print(json.dumps(res), flush=True)
+
+
+def pct_stats(xs):
+    xs = np.sort(np.asarray(xs, np.float64))
+    return {"median": round(float(np.median(xs)), 5),
+            "p10": round(float(np.percentile(xs, 10)), 5),
+            "p90": round(float(np.percentile(xs, 90)), 5)}
+
+
+def step_stats(torch, fn, steps):
+    """Per-step HIP-event times (ms) of fn on the current stream."""
+    ev = [(torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return pct_stats([a.elapsed_time(b) for a, b in ev])
+
+
+def bench_round(args, pct, synth, torch, dev):
+    """The full round: batch 128, N = 512 build, masks, acceptance walk."""
+    w = synth.TREE_WORKLOADS["round"]
+    t0 = time.time()
+    L, U, W, A = synth.tree_inputs(w)
+    log(f"round inputs in {time.time() - t0:.1f}s")
+    dL = torch.from_numpy(L).to(dev)
+    dU, dW = pct.bf16_tensor(U, dev), pct.bf16_tensor(W, dev)
+    dA = torch.from_numpy(A).to(dev)
+    del L
+    tb = pct.TreeBuilder(w.batch, w.B, w.V, w.k, w.beam_w, w.N, r=w.r,
+                         bf16=True, mask=False, device=dev)
+    o = tb.run(dL, dU, dW, dA)
+    torch.cuda.synchronize()
+    g = o.numpy()
+    tgt = torch.from_numpy(synth.targets_from_tree(
+        w.seed, g["tok"], g["parent"], g["depth"], g["n_nodes"], A, w.V, w.B,
+        synth.round_agreement(w.B))).to(dev)
+    words = (w.N + 63) // 64
+    mask = torch.empty(w.batch, w.N, words, dtype=torch.int64, device=dev)
+    vout = (torch.empty(w.batch, dtype=torch.int32, device=dev),
+            torch.empty(w.batch, w.B, dtype=torch.int32, device=dev),
+            torch.empty(w.batch, w.B + 1, dtype=torch.int32, device=dev))
+    parts = {
+        "build": lambda: tb.run(dL, dU, dW, dA),
+        "mask": lambda: pct.tree_mask(o.parent, o.n_nodes, out=mask),
+        "verify": lambda: pct.verify_accept(o.tok, o.parent, o.depth,
+                                            o.n_nodes, tgt, w.B, out=vout,
+                                            mask=mask),
+    }
+    for _ in range(args.warmup):
+        for f in parts.values():
+            f()
+    ev = {k: [] for k in parts}
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        for k, f in parts.items():
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            f()
+            b.record()
+            ev[k].append((a, b))
+    torch.cuda.synchronize()
+    out = {k: pct_stats([a.elapsed_time(b) for a, b in v])
+           for k, v in ev.items()}
+    total = sum(out[k]["median"] for k in parts)
+    tau = vout[0].cpu().numpy()
+    return {"workload": "round: batch 128, V=151936, B=16, k=8, beam 16, "
+                        "N=512, r=256 bf16; build + 512x512 masks + walk",
+            "ms": out, "round_ms_median_sum": round(total, 5),
+            "trees_per_sec": round(w.batch / (total / 1e3), 1),
+            "nodes_per_sec": round(w.batch * w.N / (total / 1e3), 1),
+            "mean_tau": float(tau.mean())}
+
+
+def bench_b7(args, pct, synth, torch, dev):
+    """Latency of one batch-1, B = 7, N = 64 build with its 64x64 mask."""
+    w = synth.TREE_WORKLOADS["b7"]
+    L, U, W, A = synth.tree_inputs(w)
+    dL = torch.from_numpy(L).to(dev)
+    dU, dW = pct.bf16_tensor(U, dev), pct.bf16_tensor(W, dev)
+    dA = torch.from_numpy(A).to(dev)
+    tb = pct.TreeBuilder(w.batch, w.B, w.V, w.k, w.beam_w, w.N, r=w.r,
+                         bf16=True, mask=True, device=dev)
+    for _ in range(args.warmup):
+        tb.run(dL, dU, dW, dA)
+    st = step_stats(torch, lambda: tb.run(dL, dU, dW, dA), max(args.steps, 20))
+    return {"workload": "b7: batch 1, V=151936, B=7, k=8, beam 8, N=64, "
+                        "r=256 bf16; build + 64x64 mask",
+            "latency_ms": st}
+
+
+def bench_adaptive_pc(args, pct, synth, torch, dev, dL, dU, dW, dA):
+    """Throughput stop on the parent-conditioned tree over the b16 inputs."""
+    w = synth.TREE_WORKLOADS["b16"]
+    a = synth.ADAPTIVE
+    cost = {k: a[k] for k in ("C_d", "c0", "c1", "c2", "c_ell")}
+    ctx = torch.from_numpy(synth.context_lengths(w.seed, w.batch)).to(dev)
+    kk = 20
+    ab = pct.AdaptivePCBuilder(w.batch, w.B, w.V, kk, kk, kk, cost, r=w.r,
+                               bf16=True, mask=True, device=dev)
+    for _ in range(args.warmup):
+        ab.run(dL, dU, dW, dA, ctx)
+    st = step_stats(torch, lambda: ab.run(dL, dU, dW, dA, ctx), args.steps)
+    ns = ab.n_star.cpu().numpy()
+    med = st["median"]
+    return {"workload": "b16 inputs (batch 32, V=151936, B=16, r=256) with "
+                        "k = beam = N = 20 (the kept tree is the best-first "
+                        "tree when n* <= 20), adaptive cost model",
+            "step_ms": st, "trees_per_sec": round(w.batch / (med / 1e3), 1),
+            "n_star_mean": float(ns.mean()), "n_star_std": float(ns.std()),
+            "n_star_max": int(ns.max())}
+
+
+def grid_and_cost(pct, torch, dL, dC, a, cost, ab_star):
+    """Budget grid search (DDTree-style fixed budgets) and the cost-model
+    fit / robustness sweep, on the adaptive workload's curves."""
+    from draft_tree_construction_markov_amd import costmodel as cm
+    fixed = pct.AdaptiveBuilder(a["batch"], a["B"], a["V"], a["n_max"], None,
+                                device=dL.device).run(dL, dC)
+
+    def curve(c):
+        return pct.throughput_curve(fixed.score, fixed.n_star, dC,
+                                    c).cpu().numpy()
+    f = curve(cost)
+    rows = np.arange(f.shape[0])
+    mean_f = f.mean(axis=0)
+    n_fix = int(np.argmax(mean_f))
+    f_ad = f[rows, ab_star]
+    grid = {"fixed_budgets": "every n in 0..1024 (one build, n_max 1024, "
+                             "no cost model; f from pct_throughput_curve)",
+            "best_fixed_budget": n_fix,
+            "mean_f_best_fixed": round(float(mean_f[n_fix]), 6),
+            "mean_f_adaptive": round(float(f_ad.mean()), 6),
+            "adaptive_gain": round(float(f_ad.mean() / mean_f[n_fix] - 1), 6),
+            "mean_f_oracle_budget_per_round": round(float(f.max(1).mean()),
+                                                    6),
+            "n_star_mean": float(ab_star.mean()),
+            "n_star_std": float(ab_star.std())}
+    rng = np.random.default_rng(7)
+    n = rng.integers(1, 1025, size=600)
+    ell = np.rint(np.exp(rng.uniform(np.log(512), np.log(32768), size=600)))
+    y = cm.predict(cost, n, ell) * (1 + 0.05 * rng.normal(size=600))
+    fit = cm.fit(n, ell, y, weights=1.0 / y ** 2)
+    models = {"fitted": fit.cost(cost["C_d"]),
+              "c1 x2": cm.perturbed(cost, {"c1": 2.0}),
+              "c_ell x0.5": cm.perturbed(cost, {"c_ell": 0.5}),
+              "c0 x0.5": cm.perturbed(cost, {"c0": 0.5}),
+              "all x1.5": cm.perturbed(cost, {k: 1.5 for k in cm.FEATURES})}
+    rob = cm.robustness(curve, cost, models)
+    costm = {"samples": "600 synthetic (n, l) latencies of the adaptive "
+                        "workload's cost model with 5% noise",
+             "fitted": {k: getattr(fit, k) for k in cm.FEATURES},
+             "true": {k: cost[k] for k in cm.FEATURES},
+             "robustness_rel_loss": {k: round(v["rel_loss"], 6)
+                                     for k, v in rob.items()}}
+    return grid, costm
 
 
 def bench_adaptive(args, pct, synth, torch, dev):
@@ -291,7 +477,9 @@ def bench_adaptive(args, pct, synth, torch, dev):
     rs_ms, rs_n = pct.profile_read(pct.PROF_ROWSTATS, -1)
     bf_ms, _ = pct.profile_read(pct.PROF_BESTFIRST, -1)
     pct.profile_reset()
+    st = step_stats(torch, lambda: ab.run(dL, dC), args.steps)
     ns = ab.n_star.cpu().numpy()
+    extra = grid_and_cost(pct, torch, dL, dC, a, cost, ns)
     bytes_rows = float(L.nbytes)
     rs_step = rs_ms / args.steps
     gbs = bytes_rows / (rs_step * 1e-3) / 1e9
@@ -299,7 +487,7 @@ def bench_adaptive(args, pct, synth, torch, dev):
                         "marginal rows, half peaked / half flat",
             "trees_per_sec": round(a["batch"] / (ms / 1e3), 1),
             "nodes_per_sec": round(float(ns.sum()) / (ms / 1e3), 1),
-            "ms_per_step": round(ms, 4),
+            "ms_per_step": round(ms, 4), "step_ms": st,
             "n_star_mean": float(ns.mean()), "n_star_std": float(ns.std()),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -310,20 +498,64 @@ def bench_adaptive(args, pct, synth, torch, dev):
                                    "rowsel_kernel pass (1024 rows/step)",
                          "ms_per_step": round(rs_step, 5),
                          "launches_per_step": rs_n // args.steps},
-            "bestfirst_ms_per_step": round(bf_ms / args.steps, 5)}
+            "bestfirst_ms_per_step": round(bf_ms / args.steps, 5)}, extra
+
+
+class one_core:
+    """Pin this process to one host core while the oracle runs."""
+
+    def __enter__(self):
+        self.saved = os.sched_getaffinity(0)
+        self.core = min(self.saved)
+        os.sched_setaffinity(0, {self.core})
+        return self
+
+    def __exit__(self, *exc):
+        os.sched_setaffinity(0, self.saved)
 
 
 def cpu_baseline(args, w, L, U, W, A):
     import oracle
     n = args.cpu_requests
-    t0 = time.perf_counter()
-    oracle.build_tree(L[:n], U, W, A[:n], w.k, w.beam_w, w.N)
-    el = time.perf_counter() - t0
+    with one_core() as c:
+        t0 = time.perf_counter()
+        oracle.build_tree(L[:n], U, W, A[:n], w.k, w.beam_w, w.N)
+        el = time.perf_counter() - t0
     return {"value": round(n / el, 4), "unit": "trees/s", "cores": 1,
             "kind": "oracle",
             "sample": f"first {n} requests of the b16 workload, tree build "
-                      f"only, single-threaded C oracle ({el:.1f}s) on "
-                      f"{cpu_model()}, nproc={os.cpu_count()}"}
+                      f"only, single-threaded C oracle ({el:.1f}s) pinned to "
+                      f"core {c.core} of {cpu_model()}, "
+                      f"nproc={os.cpu_count()}"}
+
+
+def cpu_baselines(synth):
+    """The oracle on the tiny, b7 and adaptive workloads in full, on one
+    pinned core (inputs drawn before the clock starts)."""
+    import oracle
+    out = {}
+    for name in ("tiny", "b7"):
+        w = synth.TREE_WORKLOADS[name]
+        L, U, W, A = synth.tree_inputs(w)
+        with one_core():
+            t0 = time.perf_counter()
+            oracle.build_tree(L, U, W, A, w.k, w.beam_w, w.N)
+            el = time.perf_counter() - t0
+        out[name] = {"requests": w.batch, "seconds": round(el, 4),
+                     "trees_per_sec": round(w.batch / el, 4)}
+    a = synth.ADAPTIVE
+    L, peaked, ctx = synth.adaptive_round(a["seed"], a["batch"], a["B"],
+                                          a["V"])
+    cost = {k: a[k] for k in ("C_d", "c0", "c1", "c2", "c_ell")}
+    with one_core():
+        t0 = time.perf_counter()
+        for q in range(a["batch"]):
+            oracle.adaptive(L[q], a["n_max"], int(ctx[q]), cost)
+        el = time.perf_counter() - t0
+    out["adaptive"] = {"requests": a["batch"], "seconds": round(el, 4),
+                       "trees_per_sec": round(a["batch"] / el, 4)}
+    out["cores"] = 1
+    return out
 
 
 if __name__ == "__main__":

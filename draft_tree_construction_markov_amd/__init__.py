@@ -404,13 +404,16 @@ def throughput_curve(score, n_nodes, ctx_len, cost: dict | None):
 # ---------------------------------------------------------------------------
 # pct_tree_mask / pct_verify_accept
 
-def tree_mask(parent, n_nodes) -> torch.Tensor:
+def tree_mask(parent, n_nodes, out=None) -> torch.Tensor:
     """parent [batch][N] int32, n_nodes [batch] -> mask [batch][N][words]
-    (int64 storage of the uint64 words)."""
+    (int64 storage of the uint64 words), into `out` when given."""
     dev = _dev(parent)
     batch, N = (int(x) for x in parent.shape)
     words = (N + 63) // 64
-    mask = torch.empty(batch, N, words, dtype=torch.int64, device=dev)
+    mask = out if out is not None else torch.empty(
+        batch, N, words, dtype=torch.int64, device=dev)
+    if tuple(mask.shape) != (batch, N, words) or mask.dtype != torch.int64:
+        raise ValueError("mask must be int64 [batch][N][ceil(N/64)]")
     _check(lib().pct_tree_mask(batch, N, _ptr(parent.contiguous()),
                                _ptr(n_nodes.contiguous()), _ptr(mask),
                                _stream(dev)))
