@@ -28,7 +28,8 @@ Prints one JSON line (rank 0):
                adaptive workloads timed in full
   round        batch 128, N = 512: build, 512x512 masks and the acceptance
                walk timed separately and summed (medians of per-step events)
-  b7_latency   batch 1, B = 7, N = 64 build + mask latency
+  b7_latency   batch 1, B = 7, N = 64 build + mask latency, and
+               verification of that tree with temperature sampling
   adaptive     the adaptive best-first build (batch 64, n_max 1024) with its
                row-statistics kernels (single-read pieces, their merge and
                the full-length pass) against HBM peak
@@ -374,9 +375,27 @@ def bench_b7(args, pct, synth, torch, dev):
     for _ in range(args.warmup):
         tb.run(dL, dU, dW, dA)
     st = step_stats(torch, lambda: tb.run(dL, dU, dW, dA), max(args.steps, 20))
+    # verification with temperature sampling on this tree: the target's
+    # logits after the root and after each of the 64 nodes (synthetic,
+    # generated before timing), Gumbel-max samples, then the walk
+    tl = torch.from_numpy(synth.drafter_logits(w.seed + 17, 1, w.N + 1, w.V,
+                                               3.0)).to(dev)
+    o = tb.out
+    sv = lambda: pct.verify_sample(o.tok, o.parent, o.depth, o.n_nodes, tl,  # noqa: E731
+                                   w.B, 0.8, 12345, mask=o.mask)
+    sv()
+    ss = step_stats(torch, sv, max(args.steps, 20))
+    rows = w.N + 1
     return {"workload": "b7: batch 1, V=151936, B=7, k=8, beam 8, N=64, "
                         "r=256 bf16; build + 64x64 mask",
-            "latency_ms": st}
+            "latency_ms": st,
+            "verify_sample": {"what": "65 rows of V=151936 target logits, "
+                                      "T = 0.8: Gumbel-max samples in "
+                                      "double + acceptance walk",
+                              "latency_ms": ss,
+                              "logits_GBs": round(rows * w.V * 4 /
+                                                  (ss["median"] * 1e-3) /
+                                                  1e9, 1)}}
 
 
 def bench_adaptive_pc(args, pct, synth, torch, dev, dL, dU, dW, dA):

@@ -80,6 +80,8 @@ def lib():
     L.pct_build_tree_adaptive_pc_workspace.restype = sz
     L.pct_throughput_curve.argtypes = [i32, i32, P, P, P,
                                        C.POINTER(CostModel), P, P]
+    L.pct_verify_sample.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P,
+                                    C.c_double, C.c_uint64, P, P, P, P, P]
     L.pct_profile_enable.argtypes = [i32]
     L.pct_profile_reset.argtypes = []
     L.pct_profile_read.argtypes = [i32, i64, C.POINTER(C.c_double),
@@ -97,15 +99,15 @@ def exported_symbols():
             "pct_build_tree_adaptive", "pct_build_tree_adaptive_workspace",
             "pct_build_tree_adaptive_pc",
             "pct_build_tree_adaptive_pc_workspace", "pct_throughput_curve",
-            "pct_build_tree_noalloc",
+            "pct_build_tree_noalloc", "pct_verify_sample",
             "pct_tree_mask", "pct_verify_accept", "pct_profile_enable",
             "pct_profile_reset", "pct_profile_read", "pct_status_string",
             "pct_last_error"]
 
 
 PROF_MARKOV, PROF_EXPAND, PROF_TOPN, PROF_MASK, PROF_ACCEPT, PROF_ROWTOP, \
-    PROF_INIT, PROF_ROWSTATS, PROF_BESTFIRST, PROF_FINALIZE, PROF_STOP = \
-    range(11)
+    PROF_INIT, PROF_ROWSTATS, PROF_BESTFIRST, PROF_FINALIZE, PROF_STOP, \
+    PROF_SAMPLE = range(12)
 
 
 def profile_enable(on: bool = True):
@@ -439,6 +441,30 @@ def verify_accept(tok, parent, depth, n_nodes, target, B: int, out=None,
         _ptr(mask), _ptr(target), _ptr(tau), _ptr(an), _ptr(at),
         _stream(dev)))
     return tau, an, at
+
+
+def verify_sample(tok, parent, depth, n_nodes, target_logits, B: int,
+                  temperature: float, seed: int, mask=None, out=None):
+    """Verification with temperature sampling: target_logits
+    [batch][N+1][V] float32.  Returns (sampled [batch][N+1], tau [batch],
+    accept_node [batch][B], accept_tok [batch][B+1])."""
+    dev = _dev(tok)
+    batch, N = (int(x) for x in tok.shape)
+    V = int(target_logits.shape[-1])
+    if tuple(target_logits.shape) != (batch, N + 1, V):
+        raise ValueError("target_logits must be [batch][N+1][V]")
+    if out is None:
+        out = (torch.empty(batch, N + 1, dtype=torch.int32, device=dev),
+               torch.empty(batch, dtype=torch.int32, device=dev),
+               torch.empty(batch, B, dtype=torch.int32, device=dev),
+               torch.empty(batch, B + 1, dtype=torch.int32, device=dev))
+    sm, tau, an, at = out
+    _check(lib().pct_verify_sample(
+        batch, N, B, V, _ptr(tok), _ptr(parent), _ptr(depth), _ptr(n_nodes),
+        _ptr(mask), _ptr(target_logits.contiguous()), float(temperature),
+        int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(sm), _ptr(tau), _ptr(an),
+        _ptr(at), _stream(dev)))
+    return sm, tau, an, at
 
 
 def bf16_tensor(bits, device="cuda") -> torch.Tensor:

@@ -738,4 +738,39 @@ pct_status pct_verify_accept(int32_t batch, int32_t N, int32_t B,
   return PCT_OK;
 }
 
+pct_status pct_verify_sample(int32_t batch, int32_t N, int32_t B, int32_t V,
+                             const int32_t* tok, const int32_t* parent,
+                             const int32_t* depth, const int32_t* n_nodes,
+                             const uint64_t* mask, const float* target_logits,
+                             double temperature, uint64_t seed,
+                             int32_t* sampled, int32_t* tau,
+                             int32_t* accept_node, int32_t* accept_tok,
+                             void* stream) {
+  if (batch < 1 || N < 1 || B < 1 || N > 8192 || V < 1)
+    return fail(PCT_ERR_INVALID_ARG,
+                "need batch, B, V >= 1 and 1 <= N <= 8192");
+  if (!(temperature > 0.0) || !(temperature < 1e300))
+    return fail(PCT_ERR_INVALID_ARG, "temperature must be positive and finite");
+  if (N + 1 > 65535)
+    return fail(PCT_ERR_UNSUPPORTED, "N + 1 exceeds 65535 rows");
+  if (!tok || !parent || !depth || !n_nodes || !target_logits || !sampled ||
+      !tau || !accept_node || !accept_tok)
+    return fail(PCT_ERR_INVALID_ARG, "required pointer is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  {
+    ProfScope ps(PROF_SAMPLE, batch, s);
+    e = launch_sample(batch, N + 1, V, target_logits, 1.0 / temperature,
+                      seed, n_nodes, sampled, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "sample kernel");
+  {
+    ProfScope ps(PROF_ACCEPT, batch, s);
+    e = launch_accept(batch, N, B, tok, parent, depth, n_nodes, mask, sampled,
+                      tau, accept_node, accept_tok, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "accept kernel");
+  return PCT_OK;
+}
+
 }  // extern "C"

@@ -8,6 +8,14 @@
 
 namespace pct {
 
+// the first step of the sampling generator, on the host
+static uint64_t splitmix64_host(uint64_t x) {
+  x += 0x9E3779B97F4A7C15ull;
+  x = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9ull;
+  x = (x ^ (x >> 27)) * 0x94D049BB133111EBull;
+  return x ^ (x >> 31);
+}
+
 // One thread per (request, row, 64-bit word).  Ancestors have smaller
 // indices than their descendants (nodes are in key order), so the walk up
 // from row i can stop as soon as it leaves word w.
@@ -123,6 +131,85 @@ __global__ __launch_bounds__(64) void accept_kernel(
       tau[q] = dl + 1;
     }
   }
+}
+
+// ---------------------------------------------------------------------
+// Sampled target tokens (verification with temperature sampling instead of
+// greedy decoding): row i of a request's target logits is the target's
+// distribution after node i-1 (row 0: after the root), and its token is
+// the Gumbel-max sample argmax_v (z_v / T - log(-log(u_v))), ties to the
+// lowest token.  u_v is SplitMix64 (Steele, Lea and Flood, 2014) of
+// (seed, stream = request * (N+1) + row, v): ((h >> 11) + 0.5) * 2^-53
+// with h = sm(sm(sm(seed) ^ stream) ^ v).  Keys are formed in double.
+// One workgroup per (row, request); rows past a request's nodes get -1.
+__device__ __forceinline__ uint64_t splitmix64(uint64_t x) {
+  x += 0x9E3779B97F4A7C15ull;
+  x = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9ull;
+  x = (x ^ (x >> 27)) * 0x94D049BB133111EBull;
+  return x ^ (x >> 31);
+}
+
+constexpr int kSampleThreads = 256;
+
+__global__ __launch_bounds__(kSampleThreads) void sample_kernel(
+    int N1, int V, const float* logits, double inv_t, uint64_t seed_mix,
+    const int32_t* n_nodes, int32_t* sampled) {
+  __shared__ double wkey[kSampleThreads / kWave];
+  __shared__ int wtok[kSampleThreads / kWave];
+  const int i = blockIdx.x, q = blockIdx.y, tid = threadIdx.x;
+  const int64_t row = (int64_t)q * N1 + i;
+  if (i > n_nodes[q]) {
+    if (tid == 0) sampled[row] = -1;
+    return;
+  }
+  const uint64_t key1 = splitmix64(seed_mix ^ (uint64_t)row);
+  const float* z = logits + row * V;
+  double best = -__builtin_inf();
+  int bv = 0x7fffffff;
+  for (int v = tid; v < V; v += kSampleThreads) {
+    const uint64_t h = splitmix64(key1 ^ (uint64_t)v);
+    const double u = ((double)(h >> 11) + 0.5) * (1.0 / 9007199254740992.0);
+    const double key = (double)z[v] * inv_t + (-log(-log(u)));
+    if (key > best) {  // tokens only grow within a thread
+      best = key;
+      bv = v;
+    }
+  }
+  // wave, then block arg-max by (key desc, token asc)
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const double ok = __shfl_xor(best, d, kWave);
+    const int ov = __shfl_xor(bv, d, kWave);
+    if (ok > best || (ok == best && ov < bv)) {
+      best = ok;
+      bv = ov;
+    }
+  }
+  const int lane = tid & 63, wave = tid >> 6;
+  if (lane == 0) {
+    wkey[wave] = best;
+    wtok[wave] = bv;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double b = wkey[0];
+    int t = wtok[0];
+    for (int w = 1; w < kSampleThreads / kWave; ++w)
+      if (wkey[w] > b || (wkey[w] == b && wtok[w] < t)) {
+        b = wkey[w];
+        t = wtok[w];
+      }
+    sampled[row] = t;
+  }
+}
+
+hipError_t launch_sample(int batch, int N1, int V, const float* logits,
+                         double inv_t, uint64_t seed, const int32_t* n_nodes,
+                         int32_t* sampled, hipStream_t s) {
+  hipLaunchKernelGGL(sample_kernel, dim3(N1, batch), dim3(kSampleThreads), 0,
+                     s, N1, V, logits, inv_t, splitmix64_host(seed), n_nodes,
+                     sampled);
+  return hipGetLastError();
 }
 
 hipError_t launch_mask(int batch, int N, const int32_t* parent,

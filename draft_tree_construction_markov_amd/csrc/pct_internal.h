@@ -91,7 +91,8 @@ enum ProfKind {
   PROF_ROWSTATS = 7, // adaptive: streaming log-softmax + select
   PROF_BESTFIRST = 8,// adaptive: best-first order + stop
   PROF_FINALIZE = 9, // standalone Markov call: per-parent results
-  PROF_STOP = 10     // throughput stop / curve scan
+  PROF_STOP = 10,    // throughput stop / curve scan
+  PROF_SAMPLE = 11   // sampled target tokens
 };
 
 // RAII bracket of one launch (no-op unless profiling is enabled).
@@ -222,6 +223,9 @@ struct StopArgs {
 hipError_t launch_stop_scan(int batch, const StopArgs& a, hipStream_t s);
 hipError_t launch_mask(int batch, int N, const int32_t* parent,
                        const int32_t* n_nodes, uint64_t* mask, hipStream_t s);
+hipError_t launch_sample(int batch, int N1, int V, const float* logits,
+                         double inv_t, uint64_t seed, const int32_t* n_nodes,
+                         int32_t* sampled, hipStream_t s);
 hipError_t launch_accept(int batch, int N, int B, const int32_t* tok,
                          const int32_t* parent, const int32_t* depth,
                          const int32_t* n_nodes, const uint64_t* mask,

@@ -275,6 +275,40 @@ pct_status pct_verify_accept(int32_t batch, int32_t N, int32_t B,
                              int32_t* accept_tok, void* stream);
 
 /* ------------------------------------------------------------------------
+ * pct_verify_sample -- verification with temperature sampling instead of
+ * greedy decoding.  The pages evaluate greedy decoding only ([PCT] "how
+ * well it works, in numbers") and give no sampling rule; this call takes
+ * the plainest one that keeps the target's distribution for a tree of
+ * fixed (top-k) children: the target's token after each node is a sample
+ * from softmax(target logits / T) rather than its argmax, and the walk of
+ * pct_verify_accept runs on those samples ([DSP] "one inference, from guess
+ * to confirmation": accept while the target's token is a drafted child,
+ * then the target's own token).  Every emitted token is a target sample.
+ * Sampling is Gumbel-max: token = argmax_v (z_v / T - log(-log(u_v))), ties
+ * to the lowest token, keys in double, u_v = ((h >> 11) + 0.5) * 2^-53 with
+ * h = sm(sm(sm(seed) ^ stream) ^ v), sm the SplitMix64 finaliser (Steele,
+ * Lea and Flood, 2014) and stream = request * (N+1) + row.
+ *
+ *  tok, parent, depth, n_nodes, mask  the tree, as for pct_verify_accept
+ *  target_logits  [batch][N+1][V] fp32: row 0 the target's logits after
+ *          the root, row 1+i after node i (rows past n_nodes are not read)
+ *  temperature    T > 0; seed  the generator's seed
+ *  sampled [batch][N+1] out: the sampled target tokens (-1 past n_nodes)
+ *  tau, accept_node, accept_tok  out, as for pct_verify_accept
+ * Needs no workspace.
+ * Errors: PCT_ERR_INVALID_ARG for batch, B or V < 1, N outside [1, 8192],
+ * a temperature that is not positive and finite, or null required
+ * pointers. */
+pct_status pct_verify_sample(int32_t batch, int32_t N, int32_t B, int32_t V,
+                             const int32_t* tok, const int32_t* parent,
+                             const int32_t* depth, const int32_t* n_nodes,
+                             const uint64_t* mask, const float* target_logits,
+                             double temperature, uint64_t seed,
+                             int32_t* sampled, int32_t* tau,
+                             int32_t* accept_node, int32_t* accept_tok,
+                             void* stream);
+
+/* ------------------------------------------------------------------------
  * pct_build_tree_noalloc -- for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation): pct_build_tree with the same arguments minus the workspace,
@@ -301,7 +335,8 @@ pct_status pct_build_tree_noalloc(const pct_tree_shape* shape /*host*/,
  * (units = parents of the launch), 1 per-request expand, 2 global top-N,
  * 3 mask, 4 acceptance walk, 5 seed pre-pass (units = rows), 6 depth-1
  * init, 7 adaptive row statistics (units = rows), 8 adaptive best-first +
- * stop, 9 standalone per-parent results, 10 throughput stop / curve scan.
+ * stop, 9 standalone per-parent results, 10 throughput stop / curve scan,
+ * 11 sampled target tokens.
  *  pct_profile_enable  turns recording on or off (the event pool, 8192
  *                      launches, is created on the first enable)
  *  pct_profile_reset   forgets recorded launches

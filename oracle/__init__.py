@@ -69,6 +69,10 @@ def load():
     lib.ref_stop.argtypes = [i32, P, i32, C.POINTER(CostModel), P, P, P, P]
     lib.ref_throughput_curve.argtypes = [i32, P, i32, C.POINTER(CostModel),
                                          P]
+    lib.ref_uniform.argtypes = [C.c_uint64, C.c_uint64, C.c_uint64]
+    lib.ref_uniform.restype = C.c_double
+    lib.ref_sample_targets.argtypes = [i32, i32, P, C.c_double, C.c_uint64,
+                                       C.c_uint64, P, P]
     lib.ref_mask.argtypes = [i32, i32, P, P]
     lib.ref_mask.restype = None
     lib.ref_accept.argtypes = [i32, i32, i32, P, P, P, P, P, P]
@@ -286,3 +290,21 @@ def accept(tok, parent, n_nodes: int, B: int, target):
     _check(load().ref_accept(N, n_nodes, B, _p(tok), _p(parent), _p(target),
                              _p(tau), _p(an), _p(at)), "accept")
     return int(tau[0]), an, at
+
+
+def uniform(seed: int, stream: int, idx: int) -> float:
+    return float(load().ref_uniform(seed, stream, idx))
+
+
+def sample_targets(logits, temperature: float, seed: int, stream0: int = 0):
+    """Sampled target tokens of the rows of logits [n_rows][V].  Returns
+    (tokens [n_rows], key_gap [n_rows])."""
+    z = _f32(logits)
+    n, V = z.shape
+    out = np.empty(n, np.int32)
+    gap = np.empty(n, np.float64)
+    _check(load().ref_sample_targets(n, V, _p(z), float(temperature),
+                                     int(seed), int(stream0), _p(out),
+                                     _p(gap)), "sample_targets")
+    return out, gap
+

@@ -632,3 +632,58 @@ int ref_accept(int32_t N, int32_t n_nodes, int32_t B, const int32_t* tok,
   *tau = a + 1;
   return REF_OK;
 }
+
+/* ------------------------------------------------------------------ */
+/* sampling verification                                               */
+
+/* SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
+ * generators", 2014): the finaliser applied to a counter. */
+static uint64_t sm64(uint64_t x) {
+  x += 0x9E3779B97F4A7C15ull;
+  x = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9ull;
+  x = (x ^ (x >> 27)) * 0x94D049BB133111EBull;
+  return x ^ (x >> 31);
+}
+
+double ref_uniform(uint64_t seed, uint64_t stream, uint64_t idx) {
+  const uint64_t h = sm64(sm64(sm64(seed) ^ stream) ^ idx);
+  return ((double)(h >> 11) + 0.5) * (1.0 / 9007199254740992.0);
+}
+
+/* The target's token after each node, sampled at temperature T instead of
+ * taken as the argmax (sampling rather than greedy decoding; the pages
+ * evaluate greedy decoding only).  Row i of logits [n_rows][V] is the
+ * target's distribution after node i-1 (row 0: after the root).  The sample
+ * is the Gumbel-max choice argmax_v (z_v / T + G_v), G_v = -log(-log(u_v)),
+ * u_v = the counter-based uniform of (seed, stream0 + i, v); ties go to the
+ * lowest token.  All in double; 1/T is computed once.  key_gap (optional)
+ * receives, per row, the gap between its best and second-best keys. */
+int ref_sample_targets(int32_t n_rows, int32_t V, const float* logits,
+                       double temperature, uint64_t seed, uint64_t stream0,
+                       int32_t* out, double* key_gap) {
+  if (n_rows < 0 || V < 1 || !logits || !out || !(temperature > 0.0) ||
+      !isfinite(temperature))
+    return REF_EINVAL;
+  const double inv = 1.0 / temperature;
+  for (int32_t i = 0; i < n_rows; ++i) {
+    const float* z = logits + (int64_t)i * V;
+    double best = -INFINITY, second = -INFINITY;
+    int32_t bv = 0;
+    for (int32_t v = 0; v < V; ++v) {
+      const double u = ref_uniform(seed, stream0 + (uint64_t)i, (uint64_t)v);
+      const double g = -log(-log(u));
+      const double key = (double)z[v] * inv + g;
+      if (key > best) {
+        second = best;
+        best = key;
+        bv = v;
+      } else if (key > second) {
+        second = key;
+      }
+    }
+    out[i] = bv;
+    if (key_gap) key_gap[i] = best - second;
+  }
+  return REF_OK;
+}
+

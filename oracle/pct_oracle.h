@@ -151,6 +151,18 @@ int ref_accept(int32_t N, int32_t n_nodes, int32_t B, const int32_t* tok,
                const int32_t* parent, const int32_t* target, int32_t* tau,
                int32_t* accept_node, int32_t* accept_tok);
 
+/* Counter-based uniform in (0, 1): SplitMix64 of (seed, stream, idx),
+ * ((h >> 11) + 0.5) * 2^-53 with h = sm(sm(sm(seed) ^ stream) ^ idx). */
+double ref_uniform(uint64_t seed, uint64_t stream, uint64_t idx);
+
+/* Sampled target tokens: row i of logits [n_rows][V] gives
+ * out[i] = argmax_v (z_v / T - log(-log(u(seed, stream0 + i, v)))), ties to
+ * the lowest token (Gumbel-max sampling from softmax(z / T)); key_gap
+ * (optional) [n_rows]: best minus second-best key. */
+int ref_sample_targets(int32_t n_rows, int32_t V, const float* logits,
+                       double temperature, uint64_t seed, uint64_t stream0,
+                       int32_t* out, double* key_gap);
+
 #ifdef __cplusplus
 }
 #endif

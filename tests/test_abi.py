@@ -158,3 +158,17 @@ def test_adaptive_pc_and_curve_reject_bad_arguments():
     assert lib.pct_throughput_curve(1, 4, d, None, d, None, d, None) == 1
     assert lib.pct_throughput_curve(1, 4, d, d, d, C.byref(bad), d,
                                     None) == 1
+
+
+def test_verify_sample_rejects_bad_arguments():
+    lib = pct.lib()
+    d = C.c_void_p(256)
+    args = [d] * 4
+    assert lib.pct_verify_sample(1, 4, 2, 100, *args, None, d, 0.0, 1, d, d,
+                                 d, d, None) == 1
+    assert lib.pct_verify_sample(1, 4, 2, 100, *args, None, d, float("inf"),
+                                 1, d, d, d, d, None) == 1
+    assert lib.pct_verify_sample(1, 4, 2, 0, *args, None, d, 1.0, 1, d, d, d,
+                                 d, None) == 1
+    assert lib.pct_verify_sample(1, 4, 2, 100, *args, None, None, 1.0, 1, d,
+                                 d, d, d, None) == 1
