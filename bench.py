@@ -381,8 +381,15 @@ def bench_b7(args, pct, synth, torch, dev):
     tl = torch.from_numpy(synth.drafter_logits(w.seed + 17, 1, w.N + 1, w.V,
                                                3.0)).to(dev)
     o = tb.out
+    outs = (torch.empty(1, w.N + 1, dtype=torch.int32, device=dev),
+            torch.empty(1, dtype=torch.int32, device=dev),
+            torch.empty(1, w.B, dtype=torch.int32, device=dev),
+            torch.empty(1, w.B + 1, dtype=torch.int32, device=dev))
+    sws = torch.empty(max(1, int(pct.lib().pct_verify_sample_workspace(
+        1, w.N, w.V))), dtype=torch.uint8, device=dev)
     sv = lambda: pct.verify_sample(o.tok, o.parent, o.depth, o.n_nodes, tl,  # noqa: E731
-                                   w.B, 0.8, 12345, mask=o.mask)
+                                   w.B, 0.8, 12345, mask=o.mask, out=outs,
+                                   workspace=sws)
     sv()
     ss = step_stats(torch, sv, max(args.steps, 20))
     rows = w.N + 1

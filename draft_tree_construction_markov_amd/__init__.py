@@ -81,7 +81,10 @@ def lib():
     L.pct_throughput_curve.argtypes = [i32, i32, P, P, P,
                                        C.POINTER(CostModel), P, P]
     L.pct_verify_sample.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P,
-                                    C.c_double, C.c_uint64, P, P, P, P, P]
+                                    C.c_double, C.c_uint64, P, P, P, P, P,
+                                    sz, P]
+    L.pct_verify_sample_workspace.argtypes = [i32, i32, i32]
+    L.pct_verify_sample_workspace.restype = sz
     L.pct_profile_enable.argtypes = [i32]
     L.pct_profile_reset.argtypes = []
     L.pct_profile_read.argtypes = [i32, i64, C.POINTER(C.c_double),
@@ -100,6 +103,7 @@ def exported_symbols():
             "pct_build_tree_adaptive_pc",
             "pct_build_tree_adaptive_pc_workspace", "pct_throughput_curve",
             "pct_build_tree_noalloc", "pct_verify_sample",
+            "pct_verify_sample_workspace",
             "pct_tree_mask", "pct_verify_accept", "pct_profile_enable",
             "pct_profile_reset", "pct_profile_read", "pct_status_string",
             "pct_last_error"]
@@ -444,10 +448,12 @@ def verify_accept(tok, parent, depth, n_nodes, target, B: int, out=None,
 
 
 def verify_sample(tok, parent, depth, n_nodes, target_logits, B: int,
-                  temperature: float, seed: int, mask=None, out=None):
+                  temperature: float, seed: int, mask=None, out=None,
+                  workspace=None):
     """Verification with temperature sampling: target_logits
     [batch][N+1][V] float32.  Returns (sampled [batch][N+1], tau [batch],
-    accept_node [batch][B], accept_tok [batch][B+1])."""
+    accept_node [batch][B], accept_tok [batch][B+1]).  workspace: an
+    optional uint8 device tensor reused across calls."""
     dev = _dev(tok)
     batch, N = (int(x) for x in tok.shape)
     V = int(target_logits.shape[-1])
@@ -459,11 +465,14 @@ def verify_sample(tok, parent, depth, n_nodes, target_logits, B: int,
                torch.empty(batch, B, dtype=torch.int32, device=dev),
                torch.empty(batch, B + 1, dtype=torch.int32, device=dev))
     sm, tau, an, at = out
+    nb = int(lib().pct_verify_sample_workspace(batch, N, V))
+    if workspace is None or workspace.numel() < nb:
+        workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
     _check(lib().pct_verify_sample(
         batch, N, B, V, _ptr(tok), _ptr(parent), _ptr(depth), _ptr(n_nodes),
         _ptr(mask), _ptr(target_logits.contiguous()), float(temperature),
         int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(sm), _ptr(tau), _ptr(an),
-        _ptr(at), _stream(dev)))
+        _ptr(at), _ptr(workspace), workspace.numel(), _stream(dev)))
     return sm, tau, an, at
 
 

@@ -188,11 +188,16 @@ const char* pct_last_error(void) { return g_err; }
 // ------------------------------------------------------------------------
 size_t pct_markov_logits_workspace(int32_t P, int32_t V, int32_t k) {
   if (P < 1 || V < 1 || k < 1) return 0;
-  // plan for the larger (simple) layout so that either kernel fits
-  K1Plan a = plan_k1(P, V, 256, k, PCT_BF16, true);
-  K1Plan b = plan_k1(P, V, 0, k, PCT_F32, false);
+  // the largest layout over every kernel the call may plan: the MFMA
+  // kernel at each supported rank (its shape depends on r through the LDS
+  // it needs) and the simple kernel
+  K1Plan plans[5] = {plan_k1(P, V, 32, k, PCT_BF16, true),
+                     plan_k1(P, V, 64, k, PCT_BF16, true),
+                     plan_k1(P, V, 128, k, PCT_BF16, true),
+                     plan_k1(P, V, 256, k, PCT_BF16, true),
+                     plan_k1(P, V, 0, k, PCT_F32, false)};
   size_t need = 0;
-  for (const K1Plan* pl : {&a, &b}) {
+  for (const K1Plan* pl = plans; pl != plans + 5; ++pl) {
     Carve c{nullptr};
     c.take<float>((size_t)pl->n_slices * P);
     c.take<float>((size_t)pl->n_slices * P);
@@ -738,6 +743,22 @@ pct_status pct_verify_accept(int32_t batch, int32_t N, int32_t B,
   return PCT_OK;
 }
 
+namespace {
+pct_status check_sample(int32_t batch, int32_t N, int32_t B, int32_t V) {
+  if (batch < 1 || N < 1 || B < 1 || N > 8192 || V < 1)
+    return fail(PCT_ERR_INVALID_ARG,
+                "need batch, B, V >= 1 and 1 <= N <= 8192");
+  if (batch > 65535)
+    return fail(PCT_ERR_UNSUPPORTED, "batch = %d exceeds 65535", batch);
+  return PCT_OK;
+}
+}  // namespace
+
+size_t pct_verify_sample_workspace(int32_t batch, int32_t N, int32_t V) {
+  if (batch < 1 || N < 1 || N > 8192 || V < 1 || batch > 65535) return 0;
+  return sample_workspace((int64_t)batch * (N + 1), V);
+}
+
 pct_status pct_verify_sample(int32_t batch, int32_t N, int32_t B, int32_t V,
                              const int32_t* tok, const int32_t* parent,
                              const int32_t* depth, const int32_t* n_nodes,
@@ -745,23 +766,24 @@ pct_status pct_verify_sample(int32_t batch, int32_t N, int32_t B, int32_t V,
                              double temperature, uint64_t seed,
                              int32_t* sampled, int32_t* tau,
                              int32_t* accept_node, int32_t* accept_tok,
+                             void* workspace, size_t workspace_bytes,
                              void* stream) {
-  if (batch < 1 || N < 1 || B < 1 || N > 8192 || V < 1)
-    return fail(PCT_ERR_INVALID_ARG,
-                "need batch, B, V >= 1 and 1 <= N <= 8192");
+  pct_status st = check_sample(batch, N, B, V);
+  if (st != PCT_OK) return st;
   if (!(temperature > 0.0) || !(temperature < 1e300))
     return fail(PCT_ERR_INVALID_ARG, "temperature must be positive and finite");
-  if (N + 1 > 65535)
-    return fail(PCT_ERR_UNSUPPORTED, "N + 1 exceeds 65535 rows");
   if (!tok || !parent || !depth || !n_nodes || !target_logits || !sampled ||
       !tau || !accept_node || !accept_tok)
     return fail(PCT_ERR_INVALID_ARG, "required pointer is NULL");
+  const size_t need = sample_workspace((int64_t)batch * (N + 1), V);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PCT_ERR_WORKSPACE, "workspace needs %zu bytes", need);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   {
     ProfScope ps(PROF_SAMPLE, batch, s);
     e = launch_sample(batch, N + 1, V, target_logits, 1.0 / temperature,
-                      seed, n_nodes, sampled, s);
+                      seed, n_nodes, sampled, workspace, s);
   }
   if (e != hipSuccess) return hip_fail(e, "sample kernel");
   {

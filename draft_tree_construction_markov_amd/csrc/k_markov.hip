@@ -119,49 +119,55 @@ K1Plan plan_k1(int P, int V, int r, int k, int uw_dtype, bool has_uw,
   if (r_ok) {
     pl.kind = K1_MFMA;
     pl.R16 = R16;
-    if (P <= 256) {
-      // 32 parents per wave, 8 waves: two waves share each SIMD (64 parents
-      // per wave would leave one).  Waves past the parents only load their
-      // share of each tile: with few parents the launch is bound by the
-      // tile loads, and eight waves issue them faster than one.
-      pl.NB = 1;
-      pl.NW = 8;
-    } else {
-      pl.NB = 2;
-      pl.NW = 8;
-    }
     // static LDS: two W tiles and two L row buffers; dynamic: the lists
     const size_t wbytes = (size_t)2 * 64 * (2 * R16 + 1) * 16;  // padded rows
-    auto slots_of = [&](int nw) {
+    auto slots_of = [&](int nb, int nw) {
       if (group_fp <= 0) return 0;
-      const int span = std::min(nw * pl.NB * 32, P);
+      const int span = std::min(nw * nb * 32, P);
       return (span + group_fp - 1) / group_fp + 1;
     };
-    auto lists_of = [&](int nw) {  // lists + their lengths
-      return (size_t)nw * 64 * pl.NB * (k * sizeof(ZV) + sizeof(int));
+    auto lists_of = [&](int nb, int nw) {  // lists + their lengths
+      return (size_t)nw * 64 * nb * (k * sizeof(ZV) + sizeof(int));
     };
     const size_t staged_l = (size_t)2 * kLdsRowSlots * 16 * 16;
     const size_t direct_l = (size_t)2 * 4 * 16 * 16;
-    // staged L rows when they fit kLdsRowSlots, shrinking the workgroup if
-    // needed; otherwise rows are read directly
-    int nw = pl.NW;
-    while (nw > 1 && (slots_of(nw) > kLdsRowSlots ||
-                      wbytes + staged_l + lists_of(nw) > kLdsPerCU))
-      nw /= 2;
-    if (group_fp > 0 && slots_of(nw) <= kLdsRowSlots &&
-        wbytes + staged_l + lists_of(nw) <= kLdsPerCU && nw >= 1) {
+    // Eight waves (two per SIMD, so that one's epilogue overlaps the other's
+    // MFMA chain) in this order of preference:
+    //   64 parents per wave, L rows staged in LDS (more than 256 parents);
+    //   32 parents per wave, staged L rows;
+    //   32 parents per wave, L rows read directly (large k, or groups too
+    //   small for the row slots).
+    // Measured at 640 parents with k = 20: 105 us against 362 us for two
+    // waves of 64 parents; at 128 parents of one L row each: 51 against
+    // 172 us for one-wave workgroups.  Waves past the parents only load
+    // their share of each tile: with few parents the launch is bound by
+    // the tile loads, and eight waves issue them faster than one.
+    auto fits = [&](int nb, bool staged) {
+      if (staged && (group_fp <= 0 || slots_of(nb, 8) > kLdsRowSlots))
+        return false;
+      return wbytes + (staged ? staged_l : direct_l) + lists_of(nb, 8) <=
+             kLdsPerCU;
+    };
+    auto take = [&](int nb, int nw, bool staged) {
+      pl.NB = nb;
       pl.NW = nw;
-      pl.lslots = kLdsRowSlots;
-      pl.lds = lists_of(nw);
-      pl.lds_total = wbytes + staged_l + pl.lds;
+      pl.lslots = staged ? kLdsRowSlots : 0;
+      pl.lds = lists_of(nb, nw);
+      pl.lds_total = wbytes + (staged ? staged_l : direct_l) + pl.lds;
+    };
+    if (P > 256 && fits(2, true)) {
+      take(2, 8, true);
+    } else if (fits(1, true)) {
+      take(1, 8, true);
+    } else if (fits(1, false)) {
+      take(1, 8, false);
     } else {
-      while (pl.NW > 1 && wbytes + direct_l + lists_of(pl.NW) > kLdsPerCU)
-        pl.NW /= 2;
-      pl.lslots = 0;
-      pl.lds = lists_of(pl.NW);
-      pl.lds_total = wbytes + direct_l + pl.lds;
+      // very long lists: fewer waves of 64 parents, L rows read directly
+      int nw = 4;
+      while (nw > 1 && wbytes + direct_l + lists_of(2, nw) > kLdsPerCU)
+        nw /= 2;
+      take(2, nw, false);
     }
-    if (pl.NB == 1 && pl.NW != 1 && pl.NW != 8) pl.NW = 1;
     int per_cu = (int)(kLdsPerCU / pl.lds_total);
     if (per_cu < 1) per_cu = 1;
     const int by_waves = 8 / pl.NW > 0 ? 8 / pl.NW : 1;

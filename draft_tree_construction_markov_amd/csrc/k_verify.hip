@@ -150,32 +150,20 @@ __device__ __forceinline__ uint64_t splitmix64(uint64_t x) {
 }
 
 constexpr int kSampleThreads = 256;
+constexpr int kSampleBlocks = 2048;    // workgroups a call aims for
+constexpr int kSampleMinChunk = 2048;  // logits per workgroup at least
 
-__global__ __launch_bounds__(kSampleThreads) void sample_kernel(
-    int N1, int V, const float* logits, double inv_t, uint64_t seed_mix,
-    const int32_t* n_nodes, int32_t* sampled) {
-  __shared__ double wkey[kSampleThreads / kWave];
-  __shared__ int wtok[kSampleThreads / kWave];
-  const int i = blockIdx.x, q = blockIdx.y, tid = threadIdx.x;
-  const int64_t row = (int64_t)q * N1 + i;
-  if (i > n_nodes[q]) {
-    if (tid == 0) sampled[row] = -1;
-    return;
-  }
-  const uint64_t key1 = splitmix64(seed_mix ^ (uint64_t)row);
-  const float* z = logits + row * V;
-  double best = -__builtin_inf();
-  int bv = 0x7fffffff;
-  for (int v = tid; v < V; v += kSampleThreads) {
-    const uint64_t h = splitmix64(key1 ^ (uint64_t)v);
-    const double u = ((double)(h >> 11) + 0.5) * (1.0 / 9007199254740992.0);
-    const double key = (double)z[v] * inv_t + (-log(-log(u)));
-    if (key > best) {  // tokens only grow within a thread
-      best = key;
-      bv = v;
-    }
-  }
-  // wave, then block arg-max by (key desc, token asc)
+struct SamplePart {
+  double key;
+  int32_t tok;
+  int32_t pad;
+};
+
+// Arg-max by (key desc, token asc) over the threads of one workgroup; the
+// result is valid in thread 0.
+__device__ __forceinline__ void block_argmax(double& best, int& bv,
+                                             double* wkey, int* wtok,
+                                             int tid) {
 #pragma unroll
   for (int d = 1; d < kWave; d <<= 1) {
     const double ok = __shfl_xor(best, d, kWave);
@@ -192,23 +180,113 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
   }
   __syncthreads();
   if (tid == 0) {
-    double b = wkey[0];
-    int t = wtok[0];
     for (int w = 1; w < kSampleThreads / kWave; ++w)
-      if (wkey[w] > b || (wkey[w] == b && wtok[w] < t)) {
-        b = wkey[w];
-        t = wtok[w];
+      if (wkey[w] > best || (wkey[w] == best && wtok[w] < bv)) {
+        best = wkey[w];
+        bv = wtok[w];
       }
-    sampled[row] = t;
   }
+}
+
+// Gumbel-max keys of one slice of one row (grid: slices x rows x
+// requests).  With one slice the workgroup writes the sampled token;
+// otherwise its (key, token) best goes to part[row][slice] for the merge.
+// A row whose keys are all -inf samples token 0 (the first one).
+__global__ __launch_bounds__(kSampleThreads) void sample_kernel(
+    int N1, int V, int S, int chunk, const float* logits, double inv_t,
+    uint64_t seed_mix, const int32_t* n_nodes, int32_t* sampled,
+    SamplePart* part) {
+  __shared__ double wkey[kSampleThreads / kWave];
+  __shared__ int wtok[kSampleThreads / kWave];
+  const int c = blockIdx.x, i = blockIdx.y, q = blockIdx.z,
+            tid = threadIdx.x;
+  const int64_t row = (int64_t)q * N1 + i;
+  if (i > n_nodes[q]) {
+    if (S == 1 && tid == 0) sampled[row] = -1;
+    return;
+  }
+  const uint64_t key1 = splitmix64(seed_mix ^ (uint64_t)row);
+  const float* z = logits + row * V;
+  const int v1 = min((c + 1) * chunk, V);
+  double best = -__builtin_inf();
+  int bv = 0x7fffffff;
+  for (int v = c * chunk + tid; v < v1; v += kSampleThreads) {
+    const uint64_t h = splitmix64(key1 ^ (uint64_t)v);
+    const double u = ((double)(h >> 11) + 0.5) * (1.0 / 9007199254740992.0);
+    const double key = (double)z[v] * inv_t + (-log(-log(u)));
+    if (key > best) {  // tokens only grow within a thread
+      best = key;
+      bv = v;
+    }
+  }
+  block_argmax(best, bv, wkey, wtok, tid);
+  if (tid == 0) {
+    if (S == 1)
+      sampled[row] = bv == 0x7fffffff ? 0 : bv;
+    else
+      part[row * S + c] = SamplePart{best, bv, 0};
+  }
+}
+
+// One wave per row: the arg-max of the row's S slice results.
+__global__ __launch_bounds__(256) void sample_merge_kernel(
+    int64_t rows, int N1, int S, const int32_t* n_nodes,
+    const SamplePart* part, int32_t* sampled) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int q = (int)(row / N1), i = (int)(row % N1);
+  if (i > n_nodes[q]) {
+    if (lane == 0) sampled[row] = -1;
+    return;
+  }
+  double best = -__builtin_inf();
+  int bv = 0x7fffffff;
+  for (int j = lane; j < S; j += kWave) {
+    const SamplePart p = part[row * S + j];
+    if (p.key > best || (p.key == best && p.tok < bv)) {
+      best = p.key;
+      bv = p.tok;
+    }
+  }
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const double ok = __shfl_xor(best, d, kWave);
+    const int ov = __shfl_xor(bv, d, kWave);
+    if (ok > best || (ok == best && ov < bv)) {
+      best = ok;
+      bv = ov;
+    }
+  }
+  if (lane == 0) sampled[row] = bv == 0x7fffffff ? 0 : bv;
+}
+
+int sample_slices(int64_t rows, int V) {
+  int64_t s = (kSampleBlocks + rows - 1) / rows;
+  const int64_t smax = V / kSampleMinChunk;
+  if (s > smax) s = smax;
+  return s < 1 ? 1 : (int)s;
+}
+
+size_t sample_workspace(int64_t rows, int V) {
+  const int S = sample_slices(rows, V);
+  return S > 1 ? (size_t)rows * S * sizeof(SamplePart) : 0;
 }
 
 hipError_t launch_sample(int batch, int N1, int V, const float* logits,
                          double inv_t, uint64_t seed, const int32_t* n_nodes,
-                         int32_t* sampled, hipStream_t s) {
-  hipLaunchKernelGGL(sample_kernel, dim3(N1, batch), dim3(kSampleThreads), 0,
-                     s, N1, V, logits, inv_t, splitmix64_host(seed), n_nodes,
-                     sampled);
+                         int32_t* sampled, void* ws, hipStream_t s) {
+  const int64_t rows = (int64_t)batch * N1;
+  const int S = sample_slices(rows, V);
+  const int chunk = (V + S - 1) / S;
+  SamplePart* part = static_cast<SamplePart*>(ws);
+  hipLaunchKernelGGL(sample_kernel, dim3(S, N1, batch), dim3(kSampleThreads),
+                     0, s, N1, V, S, chunk, logits, inv_t,
+                     splitmix64_host(seed), n_nodes, sampled, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 1) return e;
+  hipLaunchKernelGGL(sample_merge_kernel, dim3((unsigned)((rows + 3) / 4)),
+                     dim3(256), 0, s, rows, N1, S, n_nodes, part, sampled);
   return hipGetLastError();
 }
 

@@ -223,9 +223,14 @@ struct StopArgs {
 hipError_t launch_stop_scan(int batch, const StopArgs& a, hipStream_t s);
 hipError_t launch_mask(int batch, int N, const int32_t* parent,
                        const int32_t* n_nodes, uint64_t* mask, hipStream_t s);
+// sampled target tokens: each row is cut into sample_slices(rows, V)
+// slices; with more than one, sample_workspace(rows, V) bytes of partial
+// results are merged by a second kernel
+int sample_slices(int64_t rows, int V);
+size_t sample_workspace(int64_t rows, int V);
 hipError_t launch_sample(int batch, int N1, int V, const float* logits,
                          double inv_t, uint64_t seed, const int32_t* n_nodes,
-                         int32_t* sampled, hipStream_t s);
+                         int32_t* sampled, void* ws, hipStream_t s);
 hipError_t launch_accept(int batch, int N, int B, const int32_t* tok,
                          const int32_t* parent, const int32_t* depth,
                          const int32_t* n_nodes, const uint64_t* mask,

@@ -295,10 +295,15 @@ pct_status pct_verify_accept(int32_t batch, int32_t N, int32_t B,
  *  temperature    T > 0; seed  the generator's seed
  *  sampled [batch][N+1] out: the sampled target tokens (-1 past n_nodes)
  *  tau, accept_node, accept_tok  out, as for pct_verify_accept
- * Needs no workspace.
+ *  workspace  device memory of pct_verify_sample_workspace(batch, N, V)
+ *          bytes: when there are few rows each row is cut into slices whose
+ *          partial arg-maxes land there; may be NULL when that size is 0
+ *          (enough rows to fill the GPU one workgroup per row)
  * Errors: PCT_ERR_INVALID_ARG for batch, B or V < 1, N outside [1, 8192],
  * a temperature that is not positive and finite, or null required
- * pointers. */
+ * pointers; PCT_ERR_UNSUPPORTED for batch > 65535; PCT_ERR_WORKSPACE for a
+ * missing or short workspace. */
+size_t pct_verify_sample_workspace(int32_t batch, int32_t N, int32_t V);
 pct_status pct_verify_sample(int32_t batch, int32_t N, int32_t B, int32_t V,
                              const int32_t* tok, const int32_t* parent,
                              const int32_t* depth, const int32_t* n_nodes,
@@ -306,6 +311,7 @@ pct_status pct_verify_sample(int32_t batch, int32_t N, int32_t B, int32_t V,
                              double temperature, uint64_t seed,
                              int32_t* sampled, int32_t* tau,
                              int32_t* accept_node, int32_t* accept_tok,
+                             void* workspace, size_t workspace_bytes,
                              void* stream);
 
 /* ------------------------------------------------------------------------

@@ -165,10 +165,30 @@ def test_verify_sample_rejects_bad_arguments():
     d = C.c_void_p(256)
     args = [d] * 4
     assert lib.pct_verify_sample(1, 4, 2, 100, *args, None, d, 0.0, 1, d, d,
-                                 d, d, None) == 1
+                                 d, d, None, 0, None) == 1
     assert lib.pct_verify_sample(1, 4, 2, 100, *args, None, d, float("inf"),
-                                 1, d, d, d, d, None) == 1
+                                 1, d, d, d, d, None, 0, None) == 1
     assert lib.pct_verify_sample(1, 4, 2, 0, *args, None, d, 1.0, 1, d, d, d,
-                                 d, None) == 1
+                                 d, None, 0, None) == 1
     assert lib.pct_verify_sample(1, 4, 2, 100, *args, None, None, 1.0, 1, d,
-                                 d, d, d, None) == 1
+                                 d, d, d, None, 0, None) == 1
+    assert lib.pct_verify_sample(70000, 4, 2, 100, *args, None, d, 1.0, 1, d,
+                                 d, d, d, None, 0, None) == 2
+
+
+def test_verify_sample_workspace():
+    lib = pct.lib()
+    # few rows of a large vocabulary: rows are cut into slices whose
+    # partial results need a workspace; a missing one is an error
+    need = lib.pct_verify_sample_workspace(1, 64, 151936)
+    assert need > 0
+    d = C.c_void_p(256)
+    args = [d] * 4
+    assert lib.pct_verify_sample(1, 64, 7, 151936, *args, None, d, 1.0, 1, d,
+                                 d, d, d, None, 0, None) == 3
+    assert lib.pct_verify_sample(1, 64, 7, 151936, *args, None, d, 1.0, 1, d,
+                                 d, d, d, d, need - 1, None) == 3
+    # many rows, or a short vocabulary: one workgroup per row, no workspace
+    assert lib.pct_verify_sample_workspace(32, 256, 151936) == 0
+    assert lib.pct_verify_sample_workspace(1, 64, 1000) == 0
+    assert lib.pct_verify_sample_workspace(0, 64, 1000) == 0

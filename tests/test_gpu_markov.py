@@ -87,6 +87,39 @@ def test_lse_and_topk_match_oracle(V, r, k):
     print(f"exact {exact} near-tie {near}")
 
 
+@pytest.mark.parametrize("r,k,P", [(32, 24, 512), (256, 24, 512),
+                                   (256, 20, 640), (64, 40, 300),
+                                   (128, 64, 70)])
+def test_long_lists_across_ranks_and_parent_counts(r, k, P):
+    # long per-parent lists change the kernel's shape (parents per wave,
+    # waves per workgroup, vocabulary slices), and the shape depends on r
+    # through the LDS it needs; the workspace query must cover each of them
+    announce("markov long lists", r, k, P)
+    V = 20000
+    U, W = synth.markov_factors(31 + r, V, r, True)
+    rows = 5
+    L = synth.drafter_logits(31, 1, rows, V, 3.0, (0.5, 2.0))[0]
+    rng = np.random.default_rng(k + P)
+    toks = rng.integers(0, V, size=P).astype(np.int32)
+    lrow = rng.integers(0, rows, size=P).astype(np.int32)
+    dU, dW = dev_factors(U, W)
+    lse, tt, tl, _ = pct.markov_logits(dev_f32(L), dU, dW, dev_i32(toks),
+                                       dev_i32(lrow), k)
+    lse, tt, tl = lse.cpu().numpy(), tt.cpu().numpy(), tl.cpu().numpy()
+    near = 0
+    for p in range(0, P, 7):
+        M = oracle.markov_row(U, W, int(toks[p]))
+        ol, ot, oz, gap = oracle.row_stats(L[lrow[p]], M, k)
+        assert abs(lse[p] - ol) <= 1e-5 * max(1.0, abs(ol))
+        if np.array_equal(tt[p], ot):
+            olp = (oz - np.float32(ol)).astype(np.float32)
+            assert np.abs(tl[p] - olp).max() <= 1e-4
+        else:
+            assert gap < 1e-5, (p, tt[p], ot)
+            near += 1
+    assert near <= 2
+
+
 def test_invalid_arguments_rejected():
     announce("markov invalid args")
     t = dev_i32(np.zeros(4, np.int32))
