@@ -605,13 +605,23 @@ pct_status pct_build_tree_adaptive(int32_t batch, int32_t B, int32_t V,
                         w.ltok_f, w.llp_f, s);
   }
   if (e != hipSuccess) return hip_fail(e, "row statistics kernel");
+  const bool batched = bestfirst_batched_ok(B, V, n_max, Kf);
   {
     ProfScope ps(PROF_BESTFIRST, batch, s);
     e = launch_bestfirst(batch, B, V, n_max, Kf, Kf, Kf < V, w.ltok_f, w.llp_f,
                          ctx_len, cp, tok, parent, depth, score, n_star, phi,
-                         throughput, w.flag, 0, s);
+                         throughput, w.flag, batched ? 2 : 0, s);
   }
   if (e != hipSuccess) return hip_fail(e, "best-first kernel");
+  if (batched && Ks == Kf) {
+    // requests the batched pass could not finish, on the same lists (they
+    // are as long as the budget: every needed child rank is inside them)
+    ProfScope ps(PROF_BESTFIRST, 0, s);
+    e = launch_bestfirst(batch, B, V, n_max, Kf, Kf, Kf < V, w.ltok_f,
+                         w.llp_f, ctx_len, cp, tok, parent, depth, score,
+                         n_star, phi, throughput, w.flag, 1, s);
+    if (e != hipSuccess) return hip_fail(e, "best-first kernel");
+  }
   if (Ks > Kf) {
     // requests whose tree outgrew the short lists: full-length lists
     {

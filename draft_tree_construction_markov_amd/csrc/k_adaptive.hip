@@ -4,18 +4,27 @@
 // added one at a time and the build stops as soon as the throughput
 // (1 + Phi) / (C_d + C_v(n; l)) no longer increases).
 //
-// Two kernels:
+// Kernels:
+//  rowpart_kernel / rowmerge_kernel  single-read row statistics: each logit
+//                   row is read once, in register-resident pieces whose
+//                   maxima, exp-sums and best K are merged per row.
 //  rowsel_kernel    one workgroup per logit row: streaming log-sum-exp and
 //                   the row's best K tokens (logit desc, token asc), exact:
 //                   a pass computes per-thread bests, the K-th best of those
 //                   bounds the row's K-th best from below, a second pass
 //                   collects every element not after that bound, ranks them.
+//  bestfirst_batched_kernel  one workgroup per request: the first K <= 64
+//                   nodes of the best-first order by a threshold select
+//                   (every prefix above a provable bound, then a radix
+//                   select and exact ranking), and the stop test at every n
+//                   at once.  Requests it cannot finish are flagged.
 //  bestfirst_kernel one wave per request: lazy best-first expansion (a popped
 //                   node pushes its next sibling and its first child) over
 //                   the per-depth lists, with the stop test evaluated before
-//                   every pop.  Exact while every needed child rank is inside
-//                   the lists; a request that outgrows short lists is flagged
-//                   and rebuilt from full-length lists.
+//                   every pop; it builds the flagged requests (from
+//                   full-length lists when the short ones were outgrown).
+#include <algorithm>
+
 #include "pct_device.h"
 #include "pct_internal.h"
 
@@ -712,6 +721,423 @@ __global__ __launch_bounds__(64) void bestfirst_kernel(BestFirstArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------
+// Batched best-first (same order, same stop, no serial frontier).
+//
+// The first n nodes of the best-first order are the n best prefixes under
+// the key (score desc, parent output index asc, child rank asc), and since
+// a child never scores above its parent they form a subtree.  With the
+// needed length K <= 64 (the first pass, lists of 64), one workgroup per
+// request finds them in parallel:
+//  1. a threshold: the K-th best score among the single deviations from
+//     the greedy chain (chain node of depth d-1, then any listed token at
+//     depth d).  Those are K distinct prefixes scoring at least theta, so
+//     the K best prefixes all score at least theta;
+//  2. every prefix scoring at least theta, level by level: a node's
+//     qualifying children are a prefix of its row's sorted list (binary
+//     search), placed by a block-wide prefix sum;
+//  3. the K-th best score among those by radix select, then the exact rank
+//     of each prefix at or above it under the full key (ties resolved
+//     through the ancestors: the parent output order is the order of the
+//     parents themselves);
+//  4. the stop test at every n at once: P_n = exp(s_n) in parallel, Phi_n
+//     summed in order (the serial kernel's rounding), g(n) by ballot.
+// A request whose enumeration outgrows kBfCap nodes is flagged and rebuilt
+// by the serial kernel, as is one whose tree reaches the list length.
+
+constexpr int kBfThreads = 256;
+constexpr int kBfMaxK = 64;     // sequence length of the batched pass
+constexpr int kBfMaxRows = 64;  // depths whose lists are staged
+constexpr int kBfCap = 2048;    // prefixes at or above the threshold
+
+// Inclusive prefix sum over the 64 lanes of a wave on DPP: shifts by 1, 2,
+// 4 and 8 lanes within each row of 16, then each row adds the totals of
+// the rows before it (row_bcast:15 into rows 1 and 3, row_bcast:31 into
+// rows 2 and 3).  Every lane must be active.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);
+  return x;
+}
+
+// The k-th largest of keys[0..n) (1 <= k <= n), MSB-first radix select over
+// 8-bit digits, starting at the digit of the highest bit in which the keys
+// differ (the bits above it are common to all of them): kor / kand are
+// this thread's OR / AND of the keys it wrote.  hist has 2 x 256 ints
+// (alternate passes), oa 8, sel 2.  Every thread of the workgroup takes
+// part; the keys must be visible (a barrier after they were written).
+__device__ uint32_t bf_kth_largest(const uint32_t* keys, int n, int k,
+                                   uint32_t kor, uint32_t kand, int* hist,
+                                   int* oa, int* sel) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  kor = (uint32_t)wave_allreduce32((int)kor, [](int x, int y) { return x | y; });
+  kand = (uint32_t)wave_allreduce32((int)kand,
+                                    [](int x, int y) { return x & y; });
+  if (lane == 0) {
+    oa[wave] = (int)kor;
+    oa[4 + wave] = (int)kand;
+  }
+  hist[tid] = 0;
+  __syncthreads();
+  const uint32_t o = (uint32_t)(oa[0] | oa[1] | oa[2] | oa[3]);
+  const uint32_t a = (uint32_t)(oa[4] & oa[5] & oa[6] & oa[7]);
+  const uint32_t diff = o ^ a;
+  if (diff == 0) return a;  // every key is the same
+  const int top = 31 - __builtin_clz(diff);
+  int shift = (top / 8) * 8;
+  uint32_t mask = shift + 8 >= 32 ? 0u : ~((1u << (shift + 8)) - 1u);
+  uint32_t prefix = a & mask;
+  for (int pass = 0; shift >= 0; shift -= 8, ++pass) {
+    int* h = hist + (pass & 1) * 256;
+    hist[((pass + 1) & 1) * 256 + tid] = 0;  // the next pass's histogram
+    for (int i = tid; i < n; i += kBfThreads) {
+      const uint32_t u = keys[i];
+      if ((u & mask) == prefix) atomicAdd(&h[(u >> shift) & 255], 1);
+    }
+    __syncthreads();
+    if (tid < kWave) {
+      // lane l holds bins 255-4l .. 252-4l, in descending order
+      const int b0 = 255 - 4 * lane;
+      const int c0 = h[b0], c1 = h[b0 - 1], c2 = h[b0 - 2], c3 = h[b0 - 3];
+      const int s = c0 + c1 + c2 + c3;
+      const int inc = wave_inclusive_scan(s);
+      const int exc = inc - s;
+      if (exc < k && k <= inc) {
+        int cum = exc, b = b0;
+        if (cum + c0 < k) {
+          cum += c0;
+          b = b0 - 1;
+          if (cum + c1 < k) {
+            cum += c1;
+            b = b0 - 2;
+            if (cum + c2 < k) {
+              cum += c2;
+              b = b0 - 3;
+            }
+          }
+        }
+        sel[0] = b;
+        sel[1] = k - cum;
+      }
+    }
+    __syncthreads();
+    prefix |= (uint32_t)sel[0] << shift;
+    mask |= 0xffu << shift;
+    k = sel[1];
+  }
+  return prefix;
+}
+
+__global__ __launch_bounds__(kBfThreads) void bestfirst_batched_kernel(
+    BestFirstArgs a) {
+  __shared__ float lp[kBfMaxRows * kBfMaxK];       // later: T's scores
+  __shared__ uint32_t keys[kBfMaxRows * kBfMaxK];  // later: T, its ranks
+  __shared__ float es[kBfCap];
+  __shared__ int16_t epar[kBfCap];
+  __shared__ uint8_t erank[kBfCap];
+  __shared__ uint8_t edep[kBfCap];
+  __shared__ int16_t eout[kBfCap];
+  __shared__ float ch[kBfMaxRows + 1];
+  __shared__ int hist[512];
+  __shared__ int oa[8];
+  __shared__ int sel[2];
+  __shared__ int tcount, first_stop, s_ne, s_over;
+  __shared__ int seq[kBfMaxK];
+  __shared__ double pn[kBfMaxK];
+  __shared__ double phis[kBfMaxK + 1];
+  static_assert(kBfMaxRows * kBfMaxK >= 2 * kBfCap, "key buffer");
+
+  const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63,
+            wave = tid >> 6;
+  const int B = a.B, Kl = a.klist;
+  const int K = a.truncated ? min(a.n_max, Kl) : a.n_max;  // <= kBfMaxK
+  const int64_t rowb = (int64_t)q * B;
+
+  // 1. lists (padded to 64 entries with -inf) and the greedy chain
+  for (int i = tid; i < B * kBfMaxK; i += kBfThreads) {
+    const int d = i / kBfMaxK, j = i - d * kBfMaxK;
+    lp[i] = j < Kl ? a.llp[(rowb + d) * a.kstride + j] : neg_inf();
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float s = 0.0f;
+    ch[0] = s;
+    for (int d = 0; d < B; ++d) {
+      s = s + lp[d * kBfMaxK];
+      s = s + 0.0f;
+      ch[d + 1] = s;
+    }
+  }
+  __syncthreads();
+  const int nc = B * Kl;
+  uint32_t kor = 0, kand = 0xffffffffu;
+  for (int i = tid; i < nc; i += kBfThreads) {
+    const int d = i / Kl, j = i - d * Kl;
+    float s = ch[d] + lp[d * kBfMaxK + j];
+    s = s + 0.0f;
+    const uint32_t u = float_to_ordered(s);
+    keys[i] = u;
+    kor |= u;
+    kand &= u;
+  }
+  __syncthreads();
+  float theta = neg_inf();
+  if (nc >= K)
+    theta = ordered_to_float(
+        bf_kth_largest(keys, nc, K, kor, kand, hist, oa, sel));
+
+  // 2. every prefix scoring at least theta, level by level, in wave 0 alone
+  // (no workgroup barriers between levels)
+  if (wave == 0) {
+    int n_e = 0, lb = 0, le = 0;
+    bool over = false;
+    for (int d = 1; d <= B && !over; ++d) {
+      const int npar = d == 1 ? 1 : le - lb;
+      if (npar == 0) break;
+      const float* row = lp + (d - 1) * kBfMaxK;
+      int base = n_e;
+      for (int x0 = 0; x0 < npar; x0 += kWave) {
+        const int x = x0 + lane;
+        const bool has = x < npar;
+        const float sx = !has ? 0.0f : (d == 1 ? 0.0f : es[lb + x]);
+        int c = 0;
+        float blk[7];  // entries of the located block (block 0 when c < 8)
+#pragma unroll
+        for (int i = 0; i < 7; ++i) blk[i] = 0.0f;
+        if (has) {
+          // qualifying children are a prefix of the sorted row: the last
+          // entries of its 8-entry blocks locate the block, then the block
+          auto pass = [&](float l) {
+            float v = sx + l;
+            v = v + 0.0f;
+            return v >= theta;
+          };
+          int b = 0;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) b += pass(row[8 * k + 7]) ? 1 : 0;
+          c = 8 * b;
+          if (b < 8) {
+#pragma unroll
+            for (int i = 0; i < 7; ++i) {
+              blk[i] = row[8 * b + i];
+              c += pass(blk[i]) ? 1 : 0;
+            }
+          }
+          c = min(c, Kl);
+        }
+        const int inc = wave_inclusive_scan(c);
+        const int tot = __builtin_amdgcn_readlane(inc, 63);
+        if (base + tot > kBfCap) {
+          over = true;
+          break;
+        }
+        const int pos0 = base + inc - c;
+        const int par = d == 1 ? -1 : lb + x;
+        auto put = [&](int pos, float s0, float l, int pr, int j) {
+          float s = s0 + l;
+          s = s + 0.0f;
+          es[pos] = s;
+          epar[pos] = (int16_t)pr;
+          erank[pos] = (uint8_t)j;
+          edep[pos] = (uint8_t)d;
+        };
+        // small families: each lane writes its own children from the block
+        // entries it holds; large ones (the chain node of a flat row has up
+        // to 64): the whole wave writes one family at a time
+        if (c <= 4) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (j < c) put(pos0 + j, sx, blk[j], par, j);
+        }
+        uint64_t big = __ballot(c > 4);
+        while (big) {
+          const int L = __builtin_ctzll(big);
+          big &= big - 1;
+          const int cL = __builtin_amdgcn_readlane(c, L);
+          const int pL = __builtin_amdgcn_readlane(pos0, L);
+          const int rL = __builtin_amdgcn_readlane(par, L);
+          const float sL = __builtin_bit_cast(
+              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sx), L));
+          for (int j = lane; j < cL; j += kWave) put(pL + j, sL, row[j], rL, j);
+        }
+        base += tot;
+      }
+      // this wave's LDS writes land in order before its later reads
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      lb = n_e;
+      n_e = base;
+      le = n_e;
+    }
+    if (lane == 0) {
+      s_ne = n_e;
+      s_over = over ? 1 : 0;
+    }
+  }
+  __syncthreads();
+  const int n_e = s_ne;
+
+  int32_t* otok = a.tok + (int64_t)q * a.n_max;
+  int32_t* opar = a.parent + (int64_t)q * a.n_max;
+  int32_t* odep = a.depth + (int64_t)q * a.n_max;
+  float* osco = a.score + (int64_t)q * a.n_max;
+  if (s_over) {
+    if (tid == 0) a.flag[q] = 1;  // the serial pass builds this request
+    return;
+  }
+
+  // 3. the Ke best in exact order
+  const int Ke = min(K, n_e);
+  if (tid == 0) tcount = 0;
+  kor = 0;
+  kand = 0xffffffffu;
+  for (int i = tid; i < n_e; i += kBfThreads) {
+    const uint32_t u = float_to_ordered(es[i]);
+    keys[i] = u;
+    kor |= u;
+    kand &= u;
+  }
+  __syncthreads();
+  uint32_t tk = 0;
+  if (Ke > 0) tk = bf_kth_largest(keys, n_e, Ke, kor, kand, hist, oa, sel);
+  // T = the prefixes at or above the Ke-th best score: their ids in the
+  // upper half of the key buffer, their scores in lp (the lists are no
+  // longer needed)
+  int* tl = reinterpret_cast<int*>(keys + kBfCap);
+  float* ts = lp;
+  for (int i = tid; i < n_e; i += kBfThreads) {
+    if (keys[i] >= tk) {
+      const int o = atomicAdd(&tcount, 1);
+      tl[o] = i;
+      ts[o] = es[i];
+    }
+  }
+  __syncthreads();
+  const int nt = tcount;
+  int* trank = reinterpret_cast<int*>(keys);  // E's keys are consumed
+  for (int t = tid; t < nt; t += kBfThreads) trank[t] = 0;
+  __syncthreads();
+  // prefix y before prefix x in the best-first order, for equal scores:
+  // the parents' order, the root before any other parent
+  auto before_tied = [&](int y, int x) {
+    for (;;) {
+      const int py = epar[y], px = epar[x];
+      if (py == px) return erank[y] < erank[x];
+      if (py < 0) return true;
+      if (px < 0) return false;
+      y = py;
+      x = px;
+      const float sy = es[y], sx = es[x];
+      if (sy != sx) return sy > sx;
+    }
+  };
+  {
+    // nt ranks, each split over `parts` threads when nt is small
+    const int parts = nt > 0 && nt < kBfThreads ? kBfThreads / nt : 1;
+    for (int w = tid; w < nt * parts; w += kBfThreads) {
+      const int t = w % nt, part = w / nt;
+      const int u0 = (int)((int64_t)nt * part / parts);
+      const int u1 = (int)((int64_t)nt * (part + 1) / parts);
+      const float sx = ts[t];
+      int r = 0;
+      for (int u = u0; u < u1; ++u) {
+        const float sy = ts[u];
+        if (sy > sx)
+          ++r;
+        else if (sy == sx && u != t && before_tied(tl[u], tl[t]))
+          ++r;
+      }
+      if (r) atomicAdd(&trank[t], r);
+    }
+  }
+  __syncthreads();
+  for (int t = tid; t < nt; t += kBfThreads)
+    if (trank[t] < Ke) seq[trank[t]] = tl[t];
+  __syncthreads();
+
+  // 4. the throughput stop over the sequence
+  const double ell = a.has_cost ? (double)a.ctx_len[q] : 0.0;
+  auto D = [&](double n) {
+    return a.C_d + a.c0 + a.c1 * n + a.c2 * n * n + a.c_ell * ell * n;
+  };
+  if (tid < Ke) {
+    const int x = seq[tid];
+    eout[x] = (int16_t)tid;
+    pn[tid] = exp((double)es[x]);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double phi = 0.0;
+    phis[0] = phi;
+    for (int n = 0; n < Ke; ++n) {
+      phi += pn[n];
+      phis[n + 1] = phi;
+    }
+  }
+  __syncthreads();
+  if (tid < kWave) {
+    bool stop = false;
+    if (a.has_cost && lane < Ke) {
+      const double n = (double)lane;
+      const double g = pn[lane] * D(n) - (1.0 + phis[lane]) * (D(n + 1.0) - D(n));
+      stop = g <= 0.0;
+    }
+    const uint64_t m = __ballot(stop);
+    if (lane == 0) first_stop = m ? (int)__builtin_ctzll(m) : Ke;
+  }
+  __syncthreads();
+  int nstar = first_stop;
+  if (nstar == Ke) {
+    // no stop before the Ke-th node: the tree is exhausted, or the budget
+    // is reached, or the next node may lie past the lists
+    int64_t size = 0, pw = 1;
+    for (int d = 1; d <= B && size <= Ke; ++d) {
+      pw *= Kl;
+      size += pw;
+    }
+    if (size <= Ke) {
+    } else if (Ke >= a.n_max) {
+      nstar = a.n_max;
+    } else {
+      if (tid == 0) a.flag[q] = 1;
+      return;
+    }
+  }
+
+  for (int n = tid; n < nstar; n += kBfThreads) {
+    const int x = seq[n];
+    const int d = edep[x];
+    otok[n] = a.ltok[(rowb + d - 1) * a.kstride + erank[x]];
+    opar[n] = epar[x] < 0 ? -1 : eout[epar[x]];
+    odep[n] = d;
+    osco[n] = es[x];
+  }
+  for (int i = nstar + tid; i < a.n_max; i += kBfThreads) {
+    otok[i] = -1;
+    opar[i] = -1;
+    odep[i] = 0;
+    osco[i] = neg_inf();
+  }
+  if (tid == 0) {
+    a.flag[q] = 0;
+    a.n_star[q] = nstar;
+    const double phi = phis[nstar];
+    a.phi[q] = phi;
+    a.thr[q] = (1.0 + phi) / (a.has_cost ? D((double)nstar) : 1.0);
+  }
+}
+
+bool bestfirst_batched_ok(int B, int V, int n_max, int klist) {
+  const int K = klist < V ? std::min(n_max, klist) : n_max;
+  return K >= 1 && K <= kBfMaxK && B >= 1 && B <= kBfMaxRows &&
+         klist >= 1 && klist <= kBfMaxK;
+}
+
 hipError_t launch_rowsel(const float* L, int rows, int V, int B, int K,
                          int kstride, const int32_t* only_flagged, int vec_ok,
                          float* lse, int32_t* ltok, float* llp,
@@ -785,7 +1211,13 @@ hipError_t launch_bestfirst(int batch, int B, int V, int n_max, int klist,
   a.thr = thr;
   a.flag = flag;
   a.slow = slow;
-  hipLaunchKernelGGL(bestfirst_kernel, dim3(batch), dim3(64), 0, s, a);
+  if (slow == 2) {
+    a.slow = 0;
+    hipLaunchKernelGGL(bestfirst_batched_kernel, dim3(batch),
+                       dim3(kBfThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(bestfirst_kernel, dim3(batch), dim3(64), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -189,6 +189,11 @@ hipError_t launch_bestfirst(int batch, int B, int V, int n_max, int klist,
                             int32_t* parent, int32_t* depth, float* score,
                             int32_t* n_star, double* phi, double* thr,
                             int32_t* flag, int slow, hipStream_t s);
+// slow: 0 serial first pass (flags requests that outgrow the lists),
+// 1 serial pass over the flagged requests, 2 batched first pass (flags the
+// same requests and those whose enumeration overflows), usable when
+// bestfirst_batched_ok()
+bool bestfirst_batched_ok(int B, int V, int n_max, int klist);
 constexpr int kAdaptiveShortList = 64;  // list length of the first pass
 constexpr int kAdaptiveMaxNodes = 1024;
 // single-read row statistics: lists up to kPartMaxK, rows cut into at most

@@ -195,6 +195,57 @@ def test_uniform_single_row_closed_form():
         assert int(ab.n_star[0]) == want
 
 
+def _tie_rows(B, n_dev, n_next, V=2000):
+    """Rows with exact score ties across depths: one token of logit 0 (its
+    log-probability rounds to a few 1e-12 below 0), n_dev tokens at -30 and
+    n_next at -31 (their log-probabilities round to exactly -30 and -31),
+    the rest at -200.  Every deviation from the greedy chain, and every
+    greedy continuation after one, scores exactly -30 (or -31): the order
+    inside those groups is decided by the parents' output order alone."""
+    row = np.full(V, -200.0, np.float32)
+    row[5] = 0.0
+    row[10:10 + n_dev] = -30.0
+    row[10 + n_dev:10 + n_dev + n_next] = -31.0
+    return np.tile(row, (1, B, 1))
+
+
+def test_exact_ties_across_depths_in_order():
+    # 4 depths, 8 tokens at -30, 55 at -31: the first 64 nodes are the
+    # chain and 60 nodes of the -30 group, whose order runs through the
+    # deviations of each depth and then the greedy continuations after them
+    L = _tie_rows(4, 8, 55)
+    g, bins = run_compare(L, np.array([800], np.int32), 64, None, "ties-4")
+    assert bins["exact"] == 1
+    assert int(g["n_star"][0]) == 64
+    assert np.all(g["score"][0][4:64] == -30.0)
+    run_compare(L, np.array([800], np.int32), 64, COST, "ties-4-cost")
+
+
+def test_tie_groups_too_large_for_the_batched_pass():
+    # 16 depths with 20 tokens at -30: over 2048 prefixes reach the
+    # threshold, so the request is rebuilt by the serial pass
+    L = _tie_rows(16, 20, 43)
+    g, bins = run_compare(L, np.array([800], np.int32), 64, None, "ties-16")
+    assert bins["exact"] == 1
+    # 16 depths with 8 tokens at -30: about 1100 tied prefixes, ranked in
+    # the batched pass
+    L = _tie_rows(16, 8, 55)
+    g, bins = run_compare(L, np.array([800], np.int32), 64, None,
+                          "ties-16-small")
+    assert bins["exact"] == 1
+
+
+@pytest.mark.parametrize("B", [64, 65])
+def test_deepest_blocks(B):
+    # 64 depths (the most the batched pass stages) and 65 (serial pass)
+    rng = np.random.default_rng(B)
+    L = (rng.normal(size=(3, B, 3000)) * 3).astype(np.float32)
+    L[:, :, 7] += 12.0  # confident rows: long greedy chains
+    ctx = np.array([600, 5000, 30000], np.int32)
+    run_compare(L, ctx, 64, None, f"deep-{B}")
+    run_compare(L, ctx, 64, COST, f"deep-{B}-cost")
+
+
 def test_adaptive_rejects_bad_cost():
     L = torch.zeros(1, 2, 100, device="cuda")
     ctx = torch.zeros(1, dtype=torch.int32, device="cuda")
