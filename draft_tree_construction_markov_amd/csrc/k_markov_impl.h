@@ -155,12 +155,15 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
   const float* lrow[NB];
   int lslot[NB];
   float thr[NB], cm2[NB], ss[NB];
+  // per-parent scalars first: a wait for any of them (vmcnt counts in
+  // order) then cannot hold up the fragment loads issued after them
+  int ptk[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const int p = pw + 32 * b + col;
     const bool valid = p < a.P;
     const int pc = valid ? p : a.P - 1;
-    const int tok = min(max(a.ptok[pc], 0), a.V - 1);
+    ptk[b] = a.upack != nullptr ? 0 : min(max(a.ptok[pc], 0), a.V - 1);
     lcount[(wave * 64 + lane) * NB + b] = 0;
     int64_t row = a.plrow ? a.plrow[pc]
                           : (int64_t)(a.group_fp > 0 ? pc / a.group_fp : pc) *
@@ -169,30 +172,30 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
     row = row < 0 ? 0 : (row >= a.L_rows ? a.L_rows - 1 : row);
     lrow[b] = (!STAGED && has_L) ? a.L + row * a.lstride : nullptr;
     lslot[b] = STAGED ? pc / a.group_fp - g0 : 0;
-    if (a.upack != nullptr) {
-      // packed rows: one contiguous 1 KB load per rank step; a block past
-      // the parents is not read
-      const uint4* up = a.upack + (int64_t)((pw + 32 * b) >> 5) * R16 * 64 + lane;
-      const bool blk = pw + 32 * b < a.P;
-#pragma unroll
-      for (int kk = 0; kk < R16; ++kk) {
-        uint4 raw = blk ? up[kk * 64] : make_uint4(0, 0, 0, 0);
-        if (!valid) raw = make_uint4(0, 0, 0, 0);
-        uf[b][kk] = __builtin_bit_cast(bf16x8, raw);
-      }
-    } else {
-      const uint4* up =
-          reinterpret_cast<const uint4*>(a.U) + (int64_t)tok * CH + h;
-#pragma unroll
-      for (int kk = 0; kk < R16; ++kk) {
-        uint4 raw = up[2 * kk];
-        if (!valid) raw = make_uint4(0, 0, 0, 0);
-        uf[b][kk] = __builtin_bit_cast(bf16x8, raw);
-      }
-    }
     thr[b] = valid ? (a.theta ? a.theta[p] : neg_inf()) : pos_inf();
     cm2[b] = neg_inf();
     ss[b] = 0.f;
+  }
+  // The fragment loads are unconditional and in bounds (a block past the
+  // parents reads block 0; the packed buffer holds whole blocks), so that
+  // they and the first tile's loads are in flight together; fragments of
+  // parents past P are zeroed once both have arrived.
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    if (a.upack != nullptr) {
+      // packed rows: one contiguous 1 KB load per rank step
+      const int blk = pw + 32 * b < a.P ? (pw + 32 * b) >> 5 : 0;
+      const uint4* up = a.upack + (int64_t)blk * R16 * 64 + lane;
+#pragma unroll
+      for (int kk = 0; kk < R16; ++kk)
+        uf[b][kk] = __builtin_bit_cast(bf16x8, up[kk * 64]);
+    } else {
+      const uint4* up =
+          reinterpret_cast<const uint4*>(a.U) + (int64_t)ptk[b] * CH + h;
+#pragma unroll
+      for (int kk = 0; kk < R16; ++kk)
+        uf[b][kk] = __builtin_bit_cast(bf16x8, up[2 * kk]);
+    }
   }
 
   // Tile t -> LDS by direct global->LDS loads.  W: each wave instruction
@@ -449,6 +452,20 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
   };
   if (t0 < t1) issue(t0, w0, l0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // the fragments pass through an opaque statement here, so the compiler
+  // neither predicates their loads on the zeroing below nor waits for them
+  // before the tile loads above are issued
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const bool past = pw + 32 * b + col >= a.P;
+#pragma unroll
+    for (int kk = 0; kk < R16; ++kk) {
+      uint4 v = __builtin_bit_cast(uint4, uf[b][kk]);
+      asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+      if (past) v = make_uint4(0, 0, 0, 0);
+      uf[b][kk] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
   __syncthreads();
   for (int t = t0; t < t1; t += 2) {
     tile(t, w0, l0, w1, l1, l1);
