@@ -117,6 +117,8 @@ struct TreeWs {
   int32_t* gv;
   uint64_t* pool_key;
   uint4* upack;  // packed U rows of one depth's parents (MFMA plans only)
+  uint64_t* ckey;  // one depth's child keys (split expand)
+  float* cth;      // their seed thresholds (split expand)
 };
 
 size_t carve_tree(const pct_tree_shape* sh, const TreePlan& tp, void* ws,
@@ -142,6 +144,8 @@ size_t carve_tree(const pct_tree_shape* sh, const TreePlan& tp, void* ws,
   w.upack = c.take<uint4>(mfma ? (size_t)((tp.max_P + 31) / 32 * 32) *
                                      (sh->r / 8)
                                : 0);
+  w.ckey = c.take<uint64_t>((size_t)FB * sh->k);
+  w.cth = c.take<float>((size_t)FB * sh->k);
   return c.off;
 }
 
@@ -438,9 +442,20 @@ pct_status pct_build_tree(const pct_tree_shape* shape, const float* L,
     x.pool_key = w.pool_key;
     x.seed = sa;
     x.seed.use_seed = has_uw && sa.use_seed;
+    x.ckey = w.ckey;
+    x.cth = w.cth;
+    x.ppw = std::max(1, std::min(std::min(Fp, 32 / sh.k), 4));
     {
       ProfScope ps(PROF_EXPAND, batch, s);
-      e = launch_expand(x, s);
+      // the split form pays a second launch, which only the spread of at
+      // least 64 parents over the chip recovers (batch-1 latency is better
+      // with the single kernel)
+      if (batch * Fp >= 64 && expand_split_ok(x)) {
+        e = launch_merge(x, s);
+        if (e == hipSuccess && d < B) e = launch_beam(x, s);
+      } else {
+        e = launch_expand(x, s);
+      }
     }
     if (e != hipSuccess) return hip_fail(e, "expand kernel");
   }

@@ -824,6 +824,388 @@ __global__ __launch_bounds__(kExpandWaves * 64) void expand_kernel(
   }
 }
 
+// ---------------------------------------------------------------------
+// The expand step split in two, for bf16 factors with seeds by MFMA:
+//  merge_kernel  one wave per parent, ppw parents of one request per
+//                workgroup (ppw * k <= 32): log-normaliser and top-k of the
+//                parent's candidates, child scores and keys (the pool keys,
+//                and the request's child keys for the beam); then, for the
+//                next depth, the seed thresholds of all the workgroup's
+//                children in one MFMA block whose columns they are.  The
+//                per-parent work, which dominates the single-kernel form,
+//                spreads over the chip instead of 16 waves per request on
+//                one compute unit, and every child's threshold is ready
+//                before the beam picks the parents.
+//  beam_kernel   one workgroup per request: the Fn best child keys become
+//                the next frontier, with their thresholds and packed U rows
+//                (not launched at the last depth, whose frontier is unused).
+constexpr int kMergeMaxWaves = 4;
+
+// seed_theta_mfma spread over the four waves of a workgroup: wave w takes
+// rank steps w, w+4, ... of the MFMA chain (its fragments all loaded before
+// its MFMAs: the W rows of the seed tokens from LDS, staged by the caller;
+// the U rows of up to 32 parents straight from global memory, their tokens
+// in ptok), the partial sums meet in LDS (red: 4 x 2 x 16 x 64 floats),
+// and wave 0 finishes as seed_theta_mfma does, with the same arithmetic
+// and margin.  Every thread of the workgroup calls it; the result is
+// meaningful in wave 0 only.
+__device__ float seed_theta_mfma_split(const SeedArgs& sa, const uint4* wrows,
+                                       const int32_t* ptok, int npar,
+                                       const float* lval, const int* vt,
+                                       float* red, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, col = lane & 31;
+  const int ch = sa.r / 8, cs = ch + 1, steps = sa.r / 16;
+  const int tok = col < npar ? min(max(ptok[col], 0), sa.V - 1) : 0;
+  const uint4* ug = reinterpret_cast<const uint4*>(sa.U) + (int64_t)tok * ch;
+  uint4 wf[4], uf[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int kk = wave + 4 * i;
+    if (kk < steps) {
+      uf[i] = ug[2 * kk + h];
+      wf[i] = wrows[col * cs + 2 * kk + h];
+    }
+  }
+  f32x16 acc, aacc;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    acc[j] = 0.f;
+    aacc[j] = 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (wave + 4 * i < steps) {
+      const uint4 w4 = wf[i], u4 = uf[i];
+      const uint4 wa = make_uint4(w4.x & 0x7fff7fffu, w4.y & 0x7fff7fffu,
+                                  w4.z & 0x7fff7fffu, w4.w & 0x7fff7fffu);
+      const uint4 ua = make_uint4(u4.x & 0x7fff7fffu, u4.y & 0x7fff7fffu,
+                                  u4.z & 0x7fff7fffu, u4.w & 0x7fff7fffu);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          __builtin_bit_cast(bf16x8, w4), __builtin_bit_cast(bf16x8, u4), acc,
+          0, 0, 0);
+      aacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          __builtin_bit_cast(bf16x8, wa), __builtin_bit_cast(bf16x8, ua), aacc,
+          0, 0, 0);
+    }
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      red[((wave - 1) * 32 + j) * 64 + lane] = acc[j];
+      red[((wave - 1) * 32 + 16 + j) * 64 + lane] = aacc[j];
+    }
+  }
+  __syncthreads();
+  if (wave > 0) return 0.f;
+  // partial sums in rank-step order of the waves: the sum is the same
+  // exact products as one chain, rounded in another order (the margin
+  // bounds either)
+#pragma unroll
+  for (int w = 0; w < 3; ++w)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      acc[j] += red[(w * 32 + j) * 64 + lane];
+      aacc[j] += red[(w * 32 + 16 + j) * 64 + lane];
+    }
+  // register j holds seed token 8*(j/4) + 4h + j%4 of this column's parent
+  // (the token and logit reads all issued first, the test as a select)
+  float z[16];
+  int tv[16];
+  float lv[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int ti = 8 * (j >> 2) + 4 * h + (j & 3);
+    tv[j] = vt[ti];
+    lv[j] = lval[ti];
+  }
+  float A = 0.f, zmax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const bool ok = tv[j] >= 0;
+    const float zj = lv[j] + acc[j];
+    z[j] = ok ? zj : neg_inf();
+    A = ok ? fmaxf(A, aacc[j]) : A;
+    zmax = ok ? fmaxf(zmax, fabsf(zj)) : zmax;
+  }
+  // k-th largest of the column's 32 values (16 here, 16 in lane^32): each
+  // half sorts its 16 values (descending, a bitonic network of max/min),
+  // takes the other half's first k, and the k-th largest of the two sorted
+  // lists a, b is max over i of min(a_i, b_{k-i}) (1-based, a_0 = b_0 =
+  // +inf) -- the same value as k rounds of arg-max
+#pragma unroll
+  for (int s2 = 2; s2 <= 16; s2 <<= 1)
+#pragma unroll
+    for (int jj = s2 >> 1; jj > 0; jj >>= 1)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int l = i ^ jj;
+        if (l > i) {
+          const float x = z[i], y = z[l];
+          // descending blocks where (i & s2) == 0, ascending otherwise; the
+          // last merge (s2 = 16) is all descending
+          if ((i & s2) == 0) {
+            z[i] = fmaxf(x, y);
+            z[l] = fminf(x, y);
+          } else {
+            z[i] = fminf(x, y);
+            z[l] = fmaxf(x, y);
+          }
+        }
+      }
+  // the other half's sorted values through LDS (an index that depends on
+  // k would otherwise index registers); red is free again once wave 0 has
+  // read the partial sums
+  float* srt = red + lane * 17;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int i = 0; i < 16; ++i) srt[i] = z[i];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const float* other = red + (lane ^ 32) * 17;
+  const int k = sa.k;
+  // every read issued before any is used (clamped in-range addresses), the
+  // range test applied as a select
+  float ob[17];
+#pragma unroll
+  for (int i = 0; i <= 16; ++i) ob[i] = other[min(max(k - i - 1, 0), 15)];
+  float kth = neg_inf();
+#pragma unroll
+  for (int i = 0; i <= 16; ++i) {
+    // i values from this half, k - i from the other
+    const int jb = k - i;
+    const float ai = i == 0 ? pos_inf() : z[i - 1];
+    const float bj = jb == 0 ? pos_inf() : ob[i];
+    const float m = fmaxf(kth, fminf(ai, bj));
+    kth = (jb >= 0 && jb <= 16) ? m : kth;
+  }
+  A = fmaxf(A, swap_halves(A, lane));
+  zmax = fmaxf(zmax, swap_halves(zmax, lane));
+  const float margin = 4.f * (float)sa.r * 5.9604645e-8f * A +
+                       4.f * 1.1920929e-7f * zmax + 1e-30f;
+  return kth - margin;
+}
+
+bool expand_split_ok(const ExpandArgs& a) {
+  const SeedArgs& s = a.seed;
+  return !a.shared_stats && s.use_seed && s.U != nullptr && s.uw_bf16 &&
+         s.r % 16 == 0 && s.r <= 256 && s.k <= kSeedT &&
+         s.upack != nullptr && a.n_slices <= kStageSlices && a.ckey &&
+         a.cth && a.ppw >= 1 && a.ppw <= kMergeMaxWaves &&
+         a.ppw * a.k <= 32 && a.Fp * a.k <= kMaxCand;
+}
+
+__global__ __launch_bounds__(kMergeMaxWaves * 64) void merge_kernel(
+    ExpandArgs a) {
+  __shared__ float2 pst[kMergeMaxWaves * kStageSlices];
+  __shared__ uint4 wrows[kSeedT * kSeedRowChunks];
+  __shared__ float red[(kMergeMaxWaves - 1) * 32 * 64];  // seed partial sums
+  __shared__ float lval[kSeedT];
+  __shared__ int vt[kSeedT];
+  __shared__ int32_t ctok[32];
+  const int q = blockIdx.y, tid = threadIdx.x, lane = tid & 63,
+            wave = tid >> 6;
+  constexpr int NT = kMergeMaxWaves * 64;  // waves past the parents only stage
+  const int j0 = blockIdx.x * a.ppw;
+  const int npar = min(a.ppw, a.Fp - j0);
+  const int S = a.n_slices;
+  const int p0 = q * a.Fp + j0;
+  const bool seeds = a.d < a.B;
+  const int NC = a.Fp * a.k;
+  // 1. every independent load first: the next row's seed tokens, the
+  // partials of the workgroup's parents ([S][P] rows of consecutive
+  // parents), the first 64 candidate slots and the candidate count of this
+  // wave's parent, then the seed tokens' W rows
+  constexpr int kWIt = kSeedT * (kSeedRowChunks - 1) / NT;  // chunks/thread
+  const int ch = a.seed.r / 8, cs = ch + 1;
+  const int srow = q * a.B + a.d;
+  const int* rt = a.seed.rowtop + (int64_t)srow * kSeedT;
+  int wtok[kWIt];
+#pragma unroll
+  for (int it = 0; it < kWIt; ++it) {
+    const int i = tid + it * NT;
+    wtok[it] = (seeds && i < kSeedT * ch) ? rt[i / ch] : -1;
+  }
+  // S * npar <= kStageSlices * ppw <= 4 * NT elements: at most 4 per thread
+  constexpr int kIt = kStageSlices * kMergeMaxWaves / NT;
+  const int total = S * npar;
+  float2 pre[kIt];
+#pragma unroll
+  for (int it = 0; it < kIt; ++it) {
+    const int e = tid + it * NT;
+    pre[it] = make_float2(neg_inf(), 0.f);
+    if (e < total) {
+      const int64_t o = (int64_t)(e / npar) * a.Pstat + p0 + e % npar;
+      pre[it] = make_float2(a.part_c[o], a.part_s[o]);
+    }
+  }
+  const bool mine = wave < npar;
+  const int j = j0 + wave;
+  const int p = q * a.Fp + (mine ? j : j0);
+  float hz = neg_inf();
+  int32_t hv = 0x7fffffff;
+  if (lane < a.cap) {
+    hz = a.gz[(int64_t)p * a.cap + lane];
+    hv = a.gv[(int64_t)p * a.cap + lane];
+  }
+  const int cnt = min(a.gcnt[p], a.cap);
+  const float sp_score = a.cur.s[p];
+  const int ppid = a.cur.pid[p];
+  // the seed tokens' W rows: r/8 16-byte chunks each, every load issued
+  // before any store
+  uint4 wpre[kWIt];
+#pragma unroll
+  for (int it = 0; it < kWIt; ++it) {
+    const int i = tid + it * NT;
+    const int v = wtok[it];
+    const int vv = (v >= 0 && v < a.seed.V) ? v : 0;
+    wpre[it] = make_uint4(0, 0, 0, 0);
+    if (seeds && i < kSeedT * ch)
+      wpre[it] = reinterpret_cast<const uint4*>(a.seed.W)[(int64_t)vv * ch +
+                                                          i % ch];
+  }
+  if (seeds) {
+    if (tid < kSeedT) {
+      const int v = rt[tid];
+      const bool ok = v >= 0 && v < a.seed.V;
+      vt[tid] = ok ? v : -1;
+      lval[tid] = ok ? a.seed.L[(int64_t)srow * a.seed.lstride + v] : 0.f;
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < kIt; ++it) {
+    const int e = tid + it * NT;
+    if (e < total) pst[(e % npar) * kStageSlices + e / npar] = pre[it];
+  }
+#pragma unroll
+  for (int it = 0; it < kWIt; ++it) {
+    const int i = tid + it * NT;
+    if (seeds && i < kSeedT * ch) wrows[(i / ch) * cs + i % ch] = wpre[it];
+  }
+  __syncthreads();
+
+  // 2. one wave per parent: log-normaliser, top-k, child keys
+  if (mine) {
+    const float2* pp = pst + wave * kStageSlices;
+    const float lse =
+        wave_lse_from([&](int i) { return pp[i]; }, S, lane);
+    // the wave's partials are consumed: its LDS rows serve as scratch
+    wave_topk_rank(a.gz + (int64_t)p * a.cap, a.gv + (int64_t)p * a.cap, cnt,
+                   a.k, lane, pst + wave * kStageSlices,
+                   [&](int i, float z, int32_t v) {
+                     // log pi(v|p), never positive (see expand_kernel)
+                     const float l = fminf(z - lse, 0.f);
+                     float s = sp_score + l;
+                     s = s + 0.0f;
+                     const int c = j * a.k + i;
+                     const uint64_t key = make_key(s, ppid, v);
+                     a.pool_key[(int64_t)q * a.pool_n + a.base_d + c] = key;
+                     a.ckey[(int64_t)q * NC + c] = key;
+                     ctok[wave * a.k + i] = v;
+                   },
+                   true, hz, hv);
+  }
+  if (!seeds) return;
+  __syncthreads();
+
+  // 3. the children's seed thresholds for the next depth: their U rows are
+  // the columns of one MFMA block against the next row's seed tokens
+  const int nch = npar * a.k;
+  const float th = seed_theta_mfma_split(a.seed, wrows, ctok, nch, lval, vt,
+                                         red, tid);
+  if (wave == 0 && lane < nch) a.cth[(int64_t)q * NC + j0 * a.k + lane] = th;
+}
+
+constexpr int kBeamThreads = 1024;
+__global__ __launch_bounds__(kBeamThreads) void beam_kernel(ExpandArgs a) {
+  __shared__ __align__(16) uint64_t ckey[kMaxCand];
+  __shared__ int32_t crank[kMaxCand];
+  __shared__ int32_t bcand[kMaxCand];
+  constexpr int NT = kBeamThreads;
+  const int q = blockIdx.x, tid = threadIdx.x;
+  const int NC = a.Fp * a.k;
+  const int row = q * a.B + a.d;  // L row of depth d+1
+  for (int c = tid; c < NC; c += NT) {
+    ckey[c] = a.ckey[(int64_t)q * NC + c];
+    crank[c] = 0;
+  }
+  __syncthreads();
+  // rank of every child key (keys are distinct: (parent, token) pairs are
+  // unique); the counts are split over the threads
+  if (NC <= NT) {
+    const int parts = max(1, NT / NC);
+    const int c = tid % NC, part = tid / NC;
+    if (part < parts) {
+      const uint64_t key = ckey[c];
+      const int o0 = (int)((int64_t)NC * part / parts);
+      const int o1 = (int)((int64_t)NC * (part + 1) / parts);
+      int r = 0;
+      int o = o0;
+      // pairs of keys per 16-byte read, four reads in flight
+      if ((o0 & 1) == 0) {
+        const ulonglong2* k2 = reinterpret_cast<const ulonglong2*>(ckey);
+        for (; o + 8 <= o1; o += 8) {
+          ulonglong2 x[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) x[u] = k2[(o >> 1) + u];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) r += (x[u].x < key) + (x[u].y < key);
+        }
+      }
+      for (; o < o1; ++o) r += ckey[o] < key;
+      atomicAdd(&crank[c], r);
+    }
+  } else {
+    for (int c = tid; c < NC; c += NT) {
+      const uint64_t key = ckey[c];
+      int r = 0;
+      for (int o = 0; o < NC; ++o) r += ckey[o] < key;
+      crank[c] = r;
+    }
+  }
+  __syncthreads();
+  for (int c = tid; c < NC; c += NT) {
+    const int rank = crank[c];
+    if (rank < a.Fn) {
+      const uint64_t key = ckey[c];
+      const int o = q * a.Fn + rank;
+      a.nxt.tok[o] = key_tok(key);
+      a.nxt.pid[o] = a.base_d + c;
+      a.nxt.s[o] = key_score(key);
+      a.nxt.lrow[o] = row;
+      a.nxt.theta[o] = a.cth[(int64_t)q * NC + c];
+      if (a.gcnt_next) a.gcnt_next[o] = 0;
+      bcand[rank] = c;
+    }
+  }
+  __syncthreads();
+  // packed U rows of the next depth's parents (the fused kernel's operand
+  // order)
+  const uint4* Ug = reinterpret_cast<const uint4*>(a.seed.U);
+  const int cr = a.seed.r / 8;
+  for (int i = tid; i < a.Fn * cr; i += NT) {
+    const int jn = i / cr, c = i % cr;
+    const int tok = min(max(key_tok(ckey[bcand[jn]]), 0), a.seed.V - 1);
+    a.seed.upack[upack_index(q * a.Fn + jn, c, cr / 2)] =
+        Ug[(int64_t)tok * cr + c];
+  }
+}
+
+hipError_t launch_merge(const ExpandArgs& a, hipStream_t s) {
+  const int gx = (a.Fp + a.ppw - 1) / a.ppw;
+  hipLaunchKernelGGL(merge_kernel, dim3(gx, a.batch),
+                     dim3(kMergeMaxWaves * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_beam(const ExpandArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(beam_kernel, dim3(a.batch), dim3(kBeamThreads), 0, s, a);
+  return hipGetLastError();
+}
+
 // Global top-N of every generated child of one request.  A key's output
 // position is its rank among the request's keys in (key asc, pool id asc):
 // the number of keys that come before it.  Keys are distinct except for

@@ -157,6 +157,10 @@ struct ExpandArgs {
   int32_t* gcnt_next;  // zeroed for the next depth's parents
   uint64_t* pool_key;  // [batch][pool_n]
   SeedArgs seed;
+  // split form (merge_kernel + beam_kernel) only
+  uint64_t* ckey;  // [batch][Fp*k] this depth's child keys
+  float* cth;      // [batch][Fp*k] their seed thresholds for depth d+1
+  int ppw;         // parents per merge workgroup (ppw <= 4, ppw * k <= 32)
 };
 
 struct TopNArgs {
@@ -173,6 +177,11 @@ hipError_t launch_rowtop(const float* L, int rows, int V, int64_t lstride,
 hipError_t launch_init(int batch, int B, const int32_t* anchor, Frontier f,
                        int32_t* gcnt, const SeedArgs& sa, hipStream_t s);
 hipError_t launch_expand(const ExpandArgs& a, hipStream_t s);
+// the split form applies to bf16 factors with seeds by MFMA, staged
+// partials and one statistics row per parent
+bool expand_split_ok(const ExpandArgs& a);
+hipError_t launch_merge(const ExpandArgs& a, hipStream_t s);
+hipError_t launch_beam(const ExpandArgs& a, hipStream_t s);
 hipError_t launch_topn(const TopNArgs& a, hipStream_t s);
 hipError_t launch_finalize(int P, int k, int n_slices, const float* part_c,
                            const float* part_s, const int32_t* gcnt,
