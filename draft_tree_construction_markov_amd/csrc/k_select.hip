@@ -464,6 +464,11 @@ __device__ __forceinline__ bool seed_by_mfma(const SeedArgs& sa) {
          sa.r <= 256 && sa.k <= kSeedT;
 }
 
+__device__ float seed_theta_mfma_split(const SeedArgs& sa, const uint4* wrows,
+                                       const int32_t* ptok, int npar,
+                                       const float* lval, const int* vt,
+                                       float* red, int tid);
+
 // ---------------------------------------------------------------------
 // Depth-1 frontier: the anchor of each request.
 // Four waves stage the seed operands (their loads in flight together); the
@@ -471,12 +476,51 @@ __device__ __forceinline__ bool seed_by_mfma(const SeedArgs& sa) {
 constexpr int kInitThreads = 256;
 __global__ __launch_bounds__(kInitThreads) void init_kernel(
     int B, const int32_t* anchor, Frontier f, int32_t* gcnt, SeedArgs sa) {
+  static_assert(kInitThreads == 256, "four waves (the split seed routine)");
   __shared__ uint4 wrows[kSeedT * kSeedRowChunks];
-  __shared__ uint4 urows[32 * kSeedRowChunks];
+  __shared__ float red[3 * 32 * 64];
   __shared__ float lval[kSeedT];
   __shared__ int vt[kSeedT];
   const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const int a = anchor[q];
+  const bool mf = seed_by_mfma(sa);
+  float th = 0.f;
+  if (mf) {
+    // the seed tokens of row q*B, then their W rows (four 16-byte chunks
+    // per thread, every load issued before any store)
+    const int ch = sa.r / 8, cs = ch + 1;
+    const int* rt = sa.rowtop + (int64_t)q * B * kSeedT;
+    int wtok[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int i = tid + it * kInitThreads;
+      wtok[it] = i < kSeedT * ch ? rt[i / ch] : -1;
+    }
+    uint4 wpre[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int i = tid + it * kInitThreads;
+      const int v = wtok[it];
+      const int vv = (v >= 0 && v < sa.V) ? v : 0;
+      wpre[it] = make_uint4(0, 0, 0, 0);
+      if (i < kSeedT * ch)
+        wpre[it] =
+            reinterpret_cast<const uint4*>(sa.W)[(int64_t)vv * ch + i % ch];
+    }
+    if (tid < kSeedT) {
+      const int v = rt[tid];
+      const bool ok = v >= 0 && v < sa.V;
+      vt[tid] = ok ? v : -1;
+      lval[tid] = ok ? sa.L[(int64_t)q * B * sa.lstride + v] : 0.f;
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int i = tid + it * kInitThreads;
+      if (i < kSeedT * ch) wrows[(i / ch) * cs + i % ch] = wpre[it];
+    }
+    __syncthreads();
+    th = seed_theta_mfma_split(sa, wrows, anchor + q, 1, lval, vt, red, tid);
+  }
   if (sa.upack != nullptr) {
     // packed U row of this parent (parent q of the depth-1 frontier)
     const int ch = sa.r / 8;
@@ -485,15 +529,8 @@ __global__ __launch_bounds__(kInitThreads) void init_kernel(
     for (int c = tid; c < ch; c += kInitThreads)
       sa.upack[upack_index(q, c, ch / 2)] = urow[c];
   }
-  const bool mf = seed_by_mfma(sa);
-  if (mf) {
-    stage_seed_rows(sa, q * B, wrows, lval, vt, tid, kInitThreads);
-    stage_parent_rows(sa, anchor + q, 1, urows, tid, kInitThreads);
-    __syncthreads();
-  }
   if (tid >= 64) return;
-  const float th = mf ? seed_theta_mfma(sa, wrows, urows, lval, vt, lane)
-                      : seed_theta(sa, a, q * B, lane);
+  if (!mf) th = seed_theta(sa, a, q * B, lane);
   if (lane == 0) {
     f.tok[q] = a;
     f.pid[q] = -1;
