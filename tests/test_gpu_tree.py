@@ -117,6 +117,23 @@ def test_large_frontier_parity(batch, B, V, k, beam, N, r, reqs):
 
 
 @pytest.mark.parametrize("batch,B,V,k,beam,N,r", [
+    # frontiers of 64 parents or more take the two-kernel expand (one wave
+    # per parent, up to four parents per workgroup, the seeds of up to 32
+    # children per MFMA block): four parents of k = 4 (16 children) and a
+    # last workgroup of two; two parents of k = 16; one parent of k = 32;
+    # a split already at depth 1 (70 anchors, k = 3)
+    (24, 4, 3000, 4, 6, 40, 128),
+    (12, 3, 2500, 16, 8, 60, 64),
+    (10, 3, 2000, 32, 7, 50, 256),
+    (70, 2, 1500, 3, 5, 20, 32),
+])
+def test_two_kernel_expand_shapes(batch, B, V, k, beam, N, r):
+    L, U, W, A = _random(batch * 11 + V + k, batch, B, V, r)
+    g, o, bins = run_and_compare(L, U, W, A, k, beam, N)
+    assert bins["near"] <= max(1, batch // 16), bins
+
+
+@pytest.mark.parametrize("batch,B,V,k,beam,N,r", [
     (8, 4, 8192, 8, 16, 64, 256),     # frontiers of 128 parents, groups of 16
     (32, 3, 4096, 8, 16, 64, 256),    # 512 parents: two blocks per wave
 ])
