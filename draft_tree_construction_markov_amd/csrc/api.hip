@@ -10,10 +10,6 @@
 #include "../../include/pctree.h"
 #include "pct_internal.h"
 
-namespace pct {
-size_t topn_lds(int pool_n);
-}
-
 using namespace pct;
 
 namespace {

@@ -1337,6 +1337,306 @@ __global__ __launch_bounds__(kTopNThreads) void topn_kernel(TopNArgs a,
   }
 }
 
+// Global top-N of one request in one workgroup: a threshold select, then a
+// sort of the kept keys only.  The order is that of topn_kernel: (key asc,
+// pool id asc).
+// 1. The pool's keys go to LDS.
+// 2. Unless the whole pool is kept, a radix select over the 80-bit
+//    composite (key, pool id), one byte per pass from the top, finds where
+//    the n-th smallest lies: a pass counts the candidates (elements whose
+//    decided bytes equal the chosen ones) per value of the next byte, and a
+//    scan of the 256 counts picks the byte where the n-th falls.  It stops
+//    as soon as every candidate with the chosen byte is kept.
+// 3. The n kept elements are compacted, in any order.
+// 4. They are sorted: runs of 64 places by counting, then neighbouring runs
+//    merged level by level.  In a merge an element's place is its offset in
+//    its own run plus the number of the partner run's elements that come
+//    before it, found by binary search.
+// 5. Place = rank = output row.  A node's parent row is the place of the
+//    parent's pool id: ancestors are always kept, since a child's key comes
+//    after its parent's (its score is not larger, and on equal scores the
+//    parent's own parent has the smaller pool id).
+constexpr int kTopSelThreads = 1024;
+constexpr int kTopRun = 64;  // 2^6, the first merge level
+constexpr int kTopSelMaxLds = 160 * 1024;
+// element tag: pool id in bits 0-13, depth in bits 14-20
+constexpr uint32_t kTagId = 0x3fffu;
+
+__device__ __forceinline__ bool comp_before(uint64_t ka, uint32_t ta,
+                                            uint64_t kb, uint32_t tb) {
+  return ka < kb || (ka == kb && (ta & kTagId) < (tb & kTagId));
+}
+
+// Top `nb` bytes of the composite (key, id) against the same bytes of the
+// chosen prefix (kp, ip): -1 before, 0 equal, 1 after.
+__device__ __forceinline__ int prefix_cmp(uint64_t key, uint32_t id, int nb,
+                                          uint64_t kp, uint32_t ip) {
+  if (nb == 0) return 0;
+  if (nb <= 8) {
+    const int sh = 64 - 8 * nb;
+    const uint64_t a = key >> sh, b = kp >> sh;
+    return a < b ? -1 : (a > b ? 1 : 0);
+  }
+  if (key != kp) return key < kp ? -1 : 1;
+  const int sh = 16 - 8 * (nb - 8);
+  const uint32_t a = id >> sh, b = ip >> sh;
+  return a < b ? -1 : (a > b ? 1 : 0);
+}
+
+// byte `lv` (0 = top) of the composite (key, 16-bit id)
+__device__ __forceinline__ int comp_byte(uint64_t key, uint32_t id, int lv) {
+  return lv < 8 ? (int)((key >> (56 - 8 * lv)) & 255u)
+                : (int)((id >> (8 * (9 - lv))) & 255u);
+}
+
+// Binary searches of two elements of one thread, interleaved: on return
+// lo0 (lo1) is the first place of [lo0, lo0 + n0) ([lo1, lo1 + n1)) whose
+// element does not come before (x0, t0) ((x1, t1)).  An exhausted search
+// reads place `safe` and ignores it.
+__device__ __forceinline__ void search2(const uint64_t* k, const uint32_t* t,
+                                        int safe, int& lo0, int n0,
+                                        uint64_t x0, uint32_t t0, int& lo1,
+                                        int n1, uint64_t x1, uint32_t t1) {
+  while (n0 > 0 || n1 > 0) {
+    const int h0 = n0 >> 1, h1 = n1 >> 1;
+    const int m0 = n0 > 0 ? lo0 + h0 : safe;
+    const int m1 = n1 > 0 ? lo1 + h1 : safe;
+    const bool b0 = comp_before(k[m0], t[m0], x0, t0);
+    const bool b1 = comp_before(k[m1], t[m1], x1, t1);
+    if (n0 > 0) {
+      lo0 = b0 ? m0 + 1 : lo0;
+      n0 = b0 ? n0 - h0 - 1 : h0;
+    }
+    if (n1 > 0) {
+      lo1 = b1 ? m1 + 1 : lo1;
+      n1 = b1 ? n1 - h1 - 1 : h1;
+    }
+  }
+}
+
+__device__ __forceinline__ int sel_wave_scan(int x) {  // inclusive, 64 lanes
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // bcast:31
+  return x;
+}
+
+// hist[d] += 1 for every lane with d >= 0.  The two values held by the
+// most lanes (in early radix passes most lanes hold one of a few) are
+// added once per wave; the rest with one atomic per lane.
+__device__ __forceinline__ void hist_add(int* hist, int d, int lane) {
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const uint64_t act = __ballot(d >= 0);
+    if (act == 0) return;
+    const int f = __builtin_ctzll(act);
+    const int v = __builtin_amdgcn_readlane(d, f);
+    const uint64_t m = __ballot(d == v);
+    if (lane == f) atomicAdd(&hist[v], __popcll(m));
+    if (d == v) d = -1;
+  }
+  if (d >= 0) atomicAdd(&hist[d], 1);
+}
+
+__global__ __launch_bounds__(kTopSelThreads) void topn_select_kernel(
+    TopNArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int hist[2][256];  // alternate passes
+  __shared__ int sbase[66];
+  __shared__ int sel[4];
+  constexpr int T = kTopSelThreads;
+  const int pn = a.pool_n, n = min(a.N, pn);
+  const int ppad = (pn + 1) & ~1, npad = (n + 1) & ~1;
+  uint64_t* pk = reinterpret_cast<uint64_t*>(smem);  // pool keys
+  uint64_t* kc = pk + ppad;                          // kept, current order
+  uint64_t* kn = kc + npad;                          // kept, next order
+  uint32_t* tc = reinterpret_cast<uint32_t*>(kn + npad);
+  uint32_t* tn = tc + npad;
+  const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  for (int p = tid; p < pn; p += T) pk[p] = a.pool_key[(int64_t)q * pn + p];
+  if (tid <= a.B + 1) sbase[tid] = a.base[tid];
+  if (tid == 0) sel[3] = 0;
+  for (int i = tid; i < 512; i += T) (&hist[0][0])[i] = 0;
+  __syncthreads();
+
+  // 2. threshold: the chosen bytes (kp, ip) and how many of the bytes are
+  // decided (nb); an element is kept when its top nb bytes are not after
+  // the chosen ones
+  uint64_t kp = 0;
+  uint32_t ip = 0;
+  int nb = 0;
+  if (n < pn) {
+    int need = n;
+    for (int lv = 0; lv < 10; ++lv) {
+      int* h = hist[lv & 1];
+      // the other buffer was last read before the previous pass's second
+      // barrier: clear it for the next pass
+      for (int i = tid; i < 256; i += T) hist[(lv + 1) & 1][i] = 0;
+      for (int p0 = 0; p0 < pn; p0 += T) {
+        const int p = min(p0 + tid, pn - 1);
+        const uint64_t x = pk[p];
+        const bool cand = p0 + tid < pn &&
+                          prefix_cmp(x, (uint32_t)p, lv, kp, ip) == 0;
+        hist_add(h, cand ? comp_byte(x, (uint32_t)p, lv) : -1, lane);
+      }
+      __syncthreads();
+      if (tid < 64) {
+        const int h0 = h[4 * lane], h1 = h[4 * lane + 1],
+                  h2 = h[4 * lane + 2], h3 = h[4 * lane + 3];
+        const int incl = sel_wave_scan(h0 + h1 + h2 + h3);
+        int ex = incl - (h0 + h1 + h2 + h3);
+        if (ex < need && need <= incl) {
+          int j = 0, hj = h0;
+          if (need > ex + hj) { ex += hj; j = 1; hj = h1; }
+          if (need > ex + hj) { ex += hj; j = 2; hj = h2; }
+          if (need > ex + hj) { ex += hj; j = 3; hj = h3; }
+          sel[0] = 4 * lane + j;
+          sel[1] = ex;
+          sel[2] = hj;
+        }
+      }
+      __syncthreads();
+      const int b = sel[0], before = sel[1], hb = sel[2];
+      if (lv < 8)
+        kp |= (uint64_t)b << (56 - 8 * lv);
+      else
+        ip |= (uint32_t)b << (8 * (9 - lv));
+      need -= before;
+      nb = lv + 1;
+      if (hb == need) break;
+    }
+  }
+
+  // 3. compaction of the n kept elements, with their tags
+  for (int p0 = 0; p0 < pn; p0 += T) {
+    const int p = p0 + tid;
+    const bool keep =
+        p < pn && (nb == 0 || prefix_cmp(pk[min(p, pn - 1)], (uint32_t)p, nb,
+                                         kp, ip) <= 0);
+    const uint64_t m = __ballot(keep);
+    int w0 = 0;
+    if (lane == 0 && m) w0 = atomicAdd(&sel[3], __popcll(m));
+    w0 = __shfl(w0, 0);
+    if (keep) {
+      const int pos = w0 + __builtin_amdgcn_mbcnt_hi(
+                               (uint32_t)(m >> 32),
+                               __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      int d = 1;
+      while (d < a.B && p >= sbase[d + 1]) ++d;
+      kn[pos] = pk[p];
+      tn[pos] = (uint32_t)p | ((uint32_t)d << 14);
+    }
+  }
+  __syncthreads();
+
+  // 4a. runs of kTopRun places sorted by counting; four lanes per element
+  // (a quad), each counting a quarter of the run
+  for (int e0 = 0; e0 < n; e0 += T / 4) {
+    const int e = min(e0 + (tid >> 2), n - 1), sub = tid & 3;
+    const uint64_t x = kn[e];
+    const uint32_t tx = tn[e];
+    const int c0 = e & ~(kTopRun - 1), c1 = min(c0 + kTopRun, n);
+    int r = 0;
+#pragma unroll 4
+    for (int j = c0 + sub; j < c1; j += 4)
+      r += comp_before(kn[j], tn[j], x, tx);
+    r = quad_sum(r);
+    if (sub == 0 && e0 + (tid >> 2) < n) {
+      kc[c0 + r] = x;
+      tc[c0 + r] = tx;
+    }
+  }
+  __syncthreads();
+  const int runs = (n + kTopRun - 1) / kTopRun;
+  if (runs > 1 && runs <= 8) {
+    // 4b'. rank = offset in the own run + the elements of every other run
+    // that come before it; lane `sub` of a quad searches runs sub, sub + 4
+    for (int e0 = 0; e0 < n; e0 += T / 4) {
+      const int e = min(e0 + (tid >> 2), n - 1), sub = tid & 3;
+      const uint64_t x = kc[e];
+      const uint32_t tx = tc[e];
+      const int own = e / kTopRun;
+      const int ra = sub, rb = sub + 4;
+      int lo0 = ra * kTopRun, lo1 = rb * kTopRun;
+      const int n0 = (ra < runs && ra != own) ? min(kTopRun, n - lo0) : 0;
+      const int n1 = (rb < runs && rb != own) ? min(kTopRun, n - lo1) : 0;
+      const int s0 = lo0, s1 = lo1;
+      search2(kc, tc, e, lo0, n0, x, tx, lo1, n1, x, tx);
+      int r = (lo0 - s0) + (lo1 - s1) + (sub == 0 ? e - own * kTopRun : 0);
+      r = quad_sum(r);
+      if (sub == 0 && e0 + (tid >> 2) < n) {
+        kn[r] = x;
+        tn[r] = tx;
+      }
+    }
+    __syncthreads();
+    uint64_t* kk = kc;
+    kc = kn;
+    kn = kk;
+    uint32_t* tt = tc;
+    tc = tn;
+    tn = tt;
+  }
+  // 4b. otherwise merges; a run at this level is R = 2^lr places
+  for (int lr = 6; runs > 8 && (1 << lr) < n; ++lr) {
+    const int R = 1 << lr;
+    for (int p0 = tid; p0 < n; p0 += 2 * T) {
+      const int p1 = min(p0 + T, n - 1);  // a repeat of p0's work if past
+      const uint64_t x0 = kc[p0], x1 = kc[p1];
+      const uint32_t t0 = tc[p0], t1 = tc[p1];
+      const int m0 = p0 >> lr, m1 = p1 >> lr;
+      const int o0 = m0 ^ 1, o1 = m1 ^ 1;
+      int lo0 = o0 * R, lo1 = o1 * R;
+      const int n0 = max(0, min(lo0 + R, n) - lo0);
+      const int n1 = max(0, min(lo1 + R, n) - lo1);
+      const int s0 = lo0, s1 = lo1;
+      search2(kc, tc, p0, lo0, n0, x0, t0, lo1, n1, x1, t1);
+      const int np0 = n0 > 0 ? min(m0, o0) * R + (p0 - m0 * R) + (lo0 - s0)
+                             : p0;
+      const int np1 = n1 > 0 ? min(m1, o1) * R + (p1 - m1 * R) + (lo1 - s1)
+                             : p1;
+      kn[np0] = x0;
+      tn[np0] = t0;
+      if (p0 + T < n) {
+        kn[np1] = x1;
+        tn[np1] = t1;
+      }
+    }
+    __syncthreads();
+    uint64_t* kk = kc;
+    kc = kn;
+    kn = kk;
+    uint32_t* tt = tc;
+    tc = tn;
+    tn = tt;
+  }
+
+  // 5. rows; the place of every kept pool id, in the pool-key array (free)
+  int* rk = reinterpret_cast<int*>(pk);
+  for (int r = tid; r < n; r += T) rk[tc[r] & kTagId] = r;
+  __syncthreads();
+  for (int r = tid; r < a.N; r += T) {
+    const int64_t o = (int64_t)q * a.N + r;
+    if (r < n) {
+      const uint64_t x = kc[r];
+      const int pp = key_ppid(x);
+      a.tok[o] = key_tok(x);
+      a.parent[o] = pp < 0 ? -1 : rk[pp];
+      a.depth[o] = (int)((tc[r] >> 14) & 127u);
+      a.score[o] = key_score(x);
+    } else {
+      a.tok[o] = -1;
+      a.parent[o] = -1;
+      a.depth[o] = 0;
+      a.score[o] = neg_inf();
+    }
+  }
+  if (tid == 0) a.n_nodes[q] = n;
+}
+
 // Per-parent results of the standalone Markov-logit call.
 __global__ __launch_bounds__(256) void finalize_kernel(
     int P, int k, int S, const float* part_c, const float* part_s,
@@ -1384,7 +1684,22 @@ hipError_t launch_expand(const ExpandArgs& a, hipStream_t s) {
 
 size_t topn_lds(int pool_n) { return (size_t)((pool_n + 1) / 2) * 16; }
 
+static size_t topn_select_lds(int pool_n, int N) {
+  const size_t pp = (size_t)((pool_n + 1) & ~1);
+  const size_t n = (size_t)((std::min(N, pool_n) + 1) & ~1);
+  return 8 * pp + 24 * n;
+}
+
 hipError_t launch_topn(const TopNArgs& a, hipStream_t s) {
+  const size_t sl = topn_select_lds(a.pool_n, a.N);
+  if (a.pool_n > 0 && a.N > 0 && sl + 2048 <= kTopSelMaxLds) {
+    hipError_t e =
+        allow_lds(reinterpret_cast<const void*>(topn_select_kernel), sl);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(topn_select_kernel, dim3(a.batch), dim3(kTopSelThreads),
+                       sl, s, a);
+    return hipGetLastError();
+  }
   hipError_t e = allow_lds(reinterpret_cast<const void*>(topn_kernel),
                            topn_lds(a.pool_n));
   if (e != hipSuccess) return e;

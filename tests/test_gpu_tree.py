@@ -134,6 +134,24 @@ def test_two_kernel_expand_shapes(batch, B, V, k, beam, N, r):
 
 
 @pytest.mark.parametrize("batch,B,V,k,beam,N,r", [
+    # the global top-N selects the N smallest keys of a pool by radix
+    # select, then sorts them (runs of 64 by counting, merged level by
+    # level): 6 + 36 + 216 + 4 * 1200 = 5058 children, N = 700 (11 runs,
+    # four merge levels).  When the pool and the kept keys do not fit one
+    # workgroup's LDS, every key is ranked by counting over several
+    # workgroups: 32 + 4 * 1920 = 7712 children, N = 4200
+    (2, 7, 4000, 6, 200, 700, 64),
+    (2, 5, 4000, 32, 60, 4200, 64),
+])
+def test_top_n_sorted_and_counted(batch, B, V, k, beam, N, r):
+    L, U, W, A = _random(batch * 13 + k, batch, B, V, r)
+    g, o, bins = run_and_compare(L, U, W, A, k, beam, N)
+    # thousands of kept nodes: an fp32 score tie between two of them is
+    # binned as a near-tie
+    assert bins["near"] <= 1, bins
+
+
+@pytest.mark.parametrize("batch,B,V,k,beam,N,r", [
     (8, 4, 8192, 8, 16, 64, 256),     # frontiers of 128 parents, groups of 16
     (32, 3, 4096, 8, 16, 64, 256),    # 512 parents: two blocks per wave
 ])
