@@ -308,11 +308,15 @@ __attribute__((amdgpu_waves_per_eu(4))) void rowpart_kernel(RowPartArgs a) {
       reinterpret_cast<const float4*>(a.L + (int64_t)row * a.V);
 
   // the piece, loaded once: unconditional loads (the tail repeats the last
-  // in-range vector) so that every load is in flight before the first use
+  // in-range vector) so that every load is in flight before the first use;
+  // non-temporal, since every logit is read once
   float4 x[kPartVec];
 #pragma unroll
-  for (int i = 0; i < kPartVec; ++i)
-    x[i] = L4[min(b4 + tid + i * kPartThreads, e4 - 1)];
+  for (int i = 0; i < kPartVec; ++i) {
+    const f32x4 y = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(
+        L4 + min(b4 + tid + i * kPartThreads, e4 - 1)));
+    x[i] = make_float4(y.x, y.y, y.z, y.w);
+  }
   // vectors i < nv of this thread are inside the piece; the rest become -inf
   const int nv = (e4 - b4 - tid + kPartThreads - 1) / kPartThreads;
 #pragma unroll

@@ -234,6 +234,8 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
       __builtin_amdgcn_global_load_lds((gbl_ptr_t)(wbase + off),
                                        (lds_ptr_t)(wd + gi * 64), 16, 0, 0);
     }
+    // L rows non-temporal (aux 2): each is read once per launch, while W
+    // is read again by every depth and should stay in the caches
     if (STAGED) {
 #pragma unroll
       for (int i = 0; i < LMAX; ++i) {
@@ -241,7 +243,7 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
         if (gi * 64 < nslots * 16)
           __builtin_amdgcn_global_load_lds((gbl_ptr_t)lsrc[i],
                                            (lds_ptr_t)(ld + gi * 64), 16, 0,
-                                           0);
+                                           2);
       }
     }
   };

@@ -30,7 +30,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // contributes the kSeedT / kRowTopPieces best of those.  Any subset is a
 // valid seed; this one is close to the row's top kSeedT.
 constexpr int kRowTopPieces = 4;
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kRowTopSlots = kSeedT / kRowTopPieces;
 
 __global__ __launch_bounds__(256) void row_top_kernel(const float* L, int V,
