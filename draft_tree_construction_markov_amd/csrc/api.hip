@@ -114,7 +114,6 @@ struct TreeWs {
   uint64_t* pool_key;
   uint4* upack;  // packed U rows of one depth's parents (MFMA plans only)
   uint64_t* ckey;  // one depth's child keys (split expand)
-  float* cth;      // their seed thresholds (split expand)
 };
 
 size_t carve_tree(const pct_tree_shape* sh, const TreePlan& tp, void* ws,
@@ -141,7 +140,6 @@ size_t carve_tree(const pct_tree_shape* sh, const TreePlan& tp, void* ws,
                                      (sh->r / 8)
                                : 0);
   w.ckey = c.take<uint64_t>((size_t)FB * sh->k);
-  w.cth = c.take<float>((size_t)FB * sh->k);
   return c.off;
 }
 
@@ -439,7 +437,6 @@ pct_status pct_build_tree(const pct_tree_shape* shape, const float* L,
     x.seed = sa;
     x.seed.use_seed = has_uw && sa.use_seed;
     x.ckey = w.ckey;
-    x.cth = w.cth;
     x.ppw = std::max(1, std::min(std::min(Fp, 32 / sh.k), 4));
     {
       ProfScope ps(PROF_EXPAND, batch, s);

@@ -870,26 +870,26 @@ __global__ __launch_bounds__(kExpandWaves * 64) void expand_kernel(
 //  merge_kernel  one wave per parent, ppw parents of one request per
 //                workgroup (ppw * k <= 32): log-normaliser and top-k of the
 //                parent's candidates, child scores and keys (the pool keys,
-//                and the request's child keys for the beam); then, for the
-//                next depth, the seed thresholds of all the workgroup's
-//                children in one MFMA block whose columns they are.  The
+//                and the request's child keys for the beam).  The
 //                per-parent work, which dominates the single-kernel form,
 //                spreads over the chip instead of 16 waves per request on
-//                one compute unit, and every child's threshold is ready
-//                before the beam picks the parents.
+//                one compute unit.
 //  beam_kernel   one workgroup per request: the Fn best child keys become
-//                the next frontier, with their thresholds and packed U rows
-//                (not launched at the last depth, whose frontier is unused).
+//                the next frontier, with their seed thresholds for the next
+//                depth (the survivors' U rows as the columns of one MFMA
+//                block per 32 of them, against the next row's seed tokens,
+//                staged while the keys are ranked) and packed U rows (not
+//                launched at the last depth, whose frontier is unused).
 constexpr int kMergeMaxWaves = 4;
 
 // seed_theta_mfma spread over the four waves of a workgroup: wave w takes
 // rank steps w, w+4, ... of the MFMA chain (its fragments all loaded before
 // its MFMAs: the W rows of the seed tokens from LDS, staged by the caller;
 // the U rows of up to 32 parents straight from global memory, their tokens
-// in ptok), the partial sums meet in LDS (red: 4 x 2 x 16 x 64 floats),
+// in ptok), the partial sums meet in LDS (red: 3 x 2 x 16 x 64 floats),
 // and wave 0 finishes as seed_theta_mfma does, with the same arithmetic
-// and margin.  Every thread of the workgroup calls it; the result is
-// meaningful in wave 0 only.
+// and margin.  Every thread of the workgroup calls it (waves past the
+// fourth only join its barrier); the result is meaningful in wave 0 only.
 __device__ float seed_theta_mfma_split(const SeedArgs& sa, const uint4* wrows,
                                        const int32_t* ptok, int npar,
                                        const float* lval, const int* vt,
@@ -899,11 +899,13 @@ __device__ float seed_theta_mfma_split(const SeedArgs& sa, const uint4* wrows,
   const int ch = sa.r / 8, cs = ch + 1, steps = sa.r / 16;
   const int tok = col < npar ? min(max(ptok[col], 0), sa.V - 1) : 0;
   const uint4* ug = reinterpret_cast<const uint4*>(sa.U) + (int64_t)tok * ch;
+  // waves 0-3 split the rank steps; any further waves of the workgroup only
+  // take part in the barrier
   uint4 wf[4], uf[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int kk = wave + 4 * i;
-    if (kk < steps) {
+    if (wave < 4 && kk < steps) {
       uf[i] = ug[2 * kk + h];
       wf[i] = wrows[col * cs + 2 * kk + h];
     }
@@ -916,7 +918,7 @@ __device__ float seed_theta_mfma_split(const SeedArgs& sa, const uint4* wrows,
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if (wave + 4 * i < steps) {
+    if (wave < 4 && wave + 4 * i < steps) {
       const uint4 w4 = wf[i], u4 = uf[i];
       const uint4 wa = make_uint4(w4.x & 0x7fff7fffu, w4.y & 0x7fff7fffu,
                                   w4.z & 0x7fff7fffu, w4.w & 0x7fff7fffu);
@@ -930,7 +932,7 @@ __device__ float seed_theta_mfma_split(const SeedArgs& sa, const uint4* wrows,
           0, 0, 0);
     }
   }
-  if (wave > 0) {
+  if (wave > 0 && wave < 4) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       red[((wave - 1) * 32 + j) * 64 + lane] = acc[j];
@@ -1035,18 +1037,13 @@ bool expand_split_ok(const ExpandArgs& a) {
   return !a.shared_stats && s.use_seed && s.U != nullptr && s.uw_bf16 &&
          s.r % 16 == 0 && s.r <= 256 && s.k <= kSeedT &&
          s.upack != nullptr && a.n_slices <= kStageSlices && a.ckey &&
-         a.cth && a.ppw >= 1 && a.ppw <= kMergeMaxWaves &&
+         a.ppw >= 1 && a.ppw <= kMergeMaxWaves &&
          a.ppw * a.k <= 32 && a.Fp * a.k <= kMaxCand;
 }
 
 __global__ __launch_bounds__(kMergeMaxWaves * 64) void merge_kernel(
     ExpandArgs a) {
   __shared__ float2 pst[kMergeMaxWaves * kStageSlices];
-  __shared__ uint4 wrows[kSeedT * kSeedRowChunks];
-  __shared__ float red[(kMergeMaxWaves - 1) * 32 * 64];  // seed partial sums
-  __shared__ float lval[kSeedT];
-  __shared__ int vt[kSeedT];
-  __shared__ int32_t ctok[32];
   const int q = blockIdx.y, tid = threadIdx.x, lane = tid & 63,
             wave = tid >> 6;
   constexpr int NT = kMergeMaxWaves * 64;  // waves past the parents only stage
@@ -1054,22 +1051,10 @@ __global__ __launch_bounds__(kMergeMaxWaves * 64) void merge_kernel(
   const int npar = min(a.ppw, a.Fp - j0);
   const int S = a.n_slices;
   const int p0 = q * a.Fp + j0;
-  const bool seeds = a.d < a.B;
   const int NC = a.Fp * a.k;
-  // 1. every independent load first: the next row's seed tokens, the
-  // partials of the workgroup's parents ([S][P] rows of consecutive
-  // parents), the first 64 candidate slots and the candidate count of this
-  // wave's parent, then the seed tokens' W rows
-  constexpr int kWIt = kSeedT * (kSeedRowChunks - 1) / NT;  // chunks/thread
-  const int ch = a.seed.r / 8, cs = ch + 1;
-  const int srow = q * a.B + a.d;
-  const int* rt = a.seed.rowtop + (int64_t)srow * kSeedT;
-  int wtok[kWIt];
-#pragma unroll
-  for (int it = 0; it < kWIt; ++it) {
-    const int i = tid + it * NT;
-    wtok[it] = (seeds && i < kSeedT * ch) ? rt[i / ch] : -1;
-  }
+  // 1. every load first: the partials of the workgroup's parents ([S][P]
+  // rows of consecutive parents), the first 64 candidate slots and the
+  // candidate count of this wave's parent
   // S * npar <= kStageSlices * ppw <= 4 * NT elements: at most 4 per thread
   constexpr int kIt = kStageSlices * kMergeMaxWaves / NT;
   const int total = S * npar;
@@ -1095,36 +1080,10 @@ __global__ __launch_bounds__(kMergeMaxWaves * 64) void merge_kernel(
   const int cnt = min(a.gcnt[p], a.cap);
   const float sp_score = a.cur.s[p];
   const int ppid = a.cur.pid[p];
-  // the seed tokens' W rows: r/8 16-byte chunks each, every load issued
-  // before any store
-  uint4 wpre[kWIt];
-#pragma unroll
-  for (int it = 0; it < kWIt; ++it) {
-    const int i = tid + it * NT;
-    const int v = wtok[it];
-    const int vv = (v >= 0 && v < a.seed.V) ? v : 0;
-    wpre[it] = make_uint4(0, 0, 0, 0);
-    if (seeds && i < kSeedT * ch)
-      wpre[it] = reinterpret_cast<const uint4*>(a.seed.W)[(int64_t)vv * ch +
-                                                          i % ch];
-  }
-  if (seeds) {
-    if (tid < kSeedT) {
-      const int v = rt[tid];
-      const bool ok = v >= 0 && v < a.seed.V;
-      vt[tid] = ok ? v : -1;
-      lval[tid] = ok ? a.seed.L[(int64_t)srow * a.seed.lstride + v] : 0.f;
-    }
-  }
 #pragma unroll
   for (int it = 0; it < kIt; ++it) {
     const int e = tid + it * NT;
     if (e < total) pst[(e % npar) * kStageSlices + e / npar] = pre[it];
-  }
-#pragma unroll
-  for (int it = 0; it < kWIt; ++it) {
-    const int i = tid + it * NT;
-    if (seeds && i < kSeedT * ch) wrows[(i / ch) * cs + i % ch] = wpre[it];
   }
   __syncthreads();
 
@@ -1145,33 +1104,62 @@ __global__ __launch_bounds__(kMergeMaxWaves * 64) void merge_kernel(
                      const uint64_t key = make_key(s, ppid, v);
                      a.pool_key[(int64_t)q * a.pool_n + a.base_d + c] = key;
                      a.ckey[(int64_t)q * NC + c] = key;
-                     ctok[wave * a.k + i] = v;
                    },
                    true, hz, hv);
   }
-  if (!seeds) return;
-  __syncthreads();
-
-  // 3. the children's seed thresholds for the next depth: their U rows are
-  // the columns of one MFMA block against the next row's seed tokens
-  const int nch = npar * a.k;
-  const float th = seed_theta_mfma_split(a.seed, wrows, ctok, nch, lval, vt,
-                                         red, tid);
-  if (wave == 0 && lane < nch) a.cth[(int64_t)q * NC + j0 * a.k + lane] = th;
 }
 
-constexpr int kBeamThreads = 1024;
+constexpr int kBeamThreads = 512;  // the seed block needs > 128 registers
 __global__ __launch_bounds__(kBeamThreads) void beam_kernel(ExpandArgs a) {
   __shared__ __align__(16) uint64_t ckey[kMaxCand];
   __shared__ int32_t crank[kMaxCand];
   __shared__ int32_t bcand[kMaxCand];
+  // the next row's seed operands and the survivors' seed thresholds
+  __shared__ uint4 wrows[kSeedT * kSeedRowChunks];
+  __shared__ float red[3 * 32 * 64];
+  __shared__ float lval[kSeedT];
+  __shared__ int vt[kSeedT];
+  __shared__ int32_t stok[32];
   constexpr int NT = kBeamThreads;
   const int q = blockIdx.x, tid = threadIdx.x;
   const int NC = a.Fp * a.k;
   const int row = q * a.B + a.d;  // L row of depth d+1
+  // every independent load first: the next row's seed tokens, the child
+  // keys, then the seed tokens' W rows (16-byte chunks, kWIt per thread)
+  constexpr int kWIt = kSeedT * (kSeedRowChunks - 1) / NT;
+  const int ch = a.seed.r / 8, cs = ch + 1;
+  const int* rt = a.seed.rowtop + (int64_t)row * kSeedT;
+  int wtok[kWIt];
+#pragma unroll
+  for (int it = 0; it < kWIt; ++it) {
+    const int i = tid + it * NT;
+    wtok[it] = i < kSeedT * ch ? rt[i / ch] : -1;
+  }
   for (int c = tid; c < NC; c += NT) {
     ckey[c] = a.ckey[(int64_t)q * NC + c];
     crank[c] = 0;
+  }
+  uint4 wpre[kWIt];
+#pragma unroll
+  for (int it = 0; it < kWIt; ++it) {
+    const int i = tid + it * NT;
+    const int v = wtok[it];
+    const int vv = (v >= 0 && v < a.seed.V) ? v : 0;
+    wpre[it] = make_uint4(0, 0, 0, 0);
+    if (i < kSeedT * ch)
+      wpre[it] = reinterpret_cast<const uint4*>(a.seed.W)[(int64_t)vv * ch +
+                                                          i % ch];
+  }
+  if (tid < kSeedT) {
+    const int v = rt[tid];
+    const bool ok = v >= 0 && v < a.seed.V;
+    vt[tid] = ok ? v : -1;
+    lval[tid] = ok ? a.seed.L[(int64_t)row * a.seed.lstride + v] : 0.f;
+  }
+#pragma unroll
+  for (int it = 0; it < kWIt; ++it) {
+    const int i = tid + it * NT;
+    if (i < kSeedT * ch) wrows[(i / ch) * cs + i % ch] = wpre[it];
   }
   __syncthreads();
   // rank of every child key (keys are distinct: (parent, token) pairs are
@@ -1217,12 +1205,22 @@ __global__ __launch_bounds__(kBeamThreads) void beam_kernel(ExpandArgs a) {
       a.nxt.pid[o] = a.base_d + c;
       a.nxt.s[o] = key_score(key);
       a.nxt.lrow[o] = row;
-      a.nxt.theta[o] = a.cth[(int64_t)q * NC + c];
       if (a.gcnt_next) a.gcnt_next[o] = 0;
       bcand[rank] = c;
     }
   }
   __syncthreads();
+  // the survivors' seed thresholds for the next depth, 32 at a time: their
+  // U rows are the columns of one MFMA block against the seed tokens
+  for (int b0 = 0; b0 < a.Fn; b0 += 32) {
+    const int nb = min(32, a.Fn - b0);
+    if (tid < nb) stok[tid] = key_tok(ckey[bcand[b0 + tid]]);
+    __syncthreads();
+    const float th =
+        seed_theta_mfma_split(a.seed, wrows, stok, nb, lval, vt, red, tid);
+    if (tid < nb) a.nxt.theta[q * a.Fn + b0 + tid] = th;
+    __syncthreads();  // stok and red are rewritten by the next block
+  }
   // packed U rows of the next depth's parents (the fused kernel's operand
   // order)
   const uint4* Ug = reinterpret_cast<const uint4*>(a.seed.U);

@@ -159,7 +159,6 @@ struct ExpandArgs {
   SeedArgs seed;
   // split form (merge_kernel + beam_kernel) only
   uint64_t* ckey;  // [batch][Fp*k] this depth's child keys
-  float* cth;      // [batch][Fp*k] their seed thresholds for depth d+1
   int ppw;         // parents per merge workgroup (ppw <= 4, ppw * k <= 32)
 };
 
