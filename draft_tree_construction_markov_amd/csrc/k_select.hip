@@ -471,7 +471,8 @@ __device__ __forceinline__ bool seed_by_mfma(const SeedArgs& sa) {
 __device__ float seed_theta_mfma_split(const SeedArgs& sa, const uint4* wrows,
                                        const int32_t* ptok, int npar,
                                        const float* lval, const int* vt,
-                                       float* red, int tid);
+                                       float* red, int tid,
+                                       uint4* upack = nullptr, int pbase = 0);
 
 // ---------------------------------------------------------------------
 // Depth-1 frontier: the anchor of each request.
@@ -523,9 +524,12 @@ __global__ __launch_bounds__(kInitThreads) void init_kernel(
       if (i < kSeedT * ch) wrows[(i / ch) * cs + i % ch] = wpre[it];
     }
     __syncthreads();
-    th = seed_theta_mfma_split(sa, wrows, anchor + q, 1, lval, vt, red, tid);
+    // with the packed U row of this parent (parent q of the depth-1
+    // frontier), which the MFMA block loads anyway
+    th = seed_theta_mfma_split(sa, wrows, anchor + q, 1, lval, vt, red, tid,
+                               sa.upack, q);
   }
-  if (sa.upack != nullptr) {
+  if (!mf && sa.upack != nullptr) {
     // packed U row of this parent (parent q of the depth-1 frontier)
     const int ch = sa.r / 8;
     const uint4* urow = reinterpret_cast<const uint4*>(sa.U) +
@@ -893,7 +897,8 @@ constexpr int kMergeMaxWaves = 4;
 __device__ float seed_theta_mfma_split(const SeedArgs& sa, const uint4* wrows,
                                        const int32_t* ptok, int npar,
                                        const float* lval, const int* vt,
-                                       float* red, int tid) {
+                                       float* red, int tid, uint4* upack,
+                                       int pbase) {
   const int lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, col = lane & 31;
   const int ch = sa.r / 8, cs = ch + 1, steps = sa.r / 16;
@@ -930,6 +935,17 @@ __device__ float seed_theta_mfma_split(const SeedArgs& sa, const uint4* wrows,
       aacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
           __builtin_bit_cast(bf16x8, wa), __builtin_bit_cast(bf16x8, ua), aacc,
           0, 0, 0);
+    }
+  }
+  // the parents' U rows pass through these registers whole: written
+  // packed in the fused kernel's operand order when asked for (parent
+  // pbase + col)
+  if (upack != nullptr && col < npar) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kk = wave + 4 * i;
+      if (wave < 4 && kk < steps)
+        upack[upack_index(pbase + col, 2 * kk + h, steps)] = uf[i];
     }
   }
   if (wave > 0 && wave < 4) {
@@ -1216,20 +1232,13 @@ __global__ __launch_bounds__(kBeamThreads) void beam_kernel(ExpandArgs a) {
     const int nb = min(32, a.Fn - b0);
     if (tid < nb) stok[tid] = key_tok(ckey[bcand[b0 + tid]]);
     __syncthreads();
-    const float th =
-        seed_theta_mfma_split(a.seed, wrows, stok, nb, lval, vt, red, tid);
+    // with the packed U rows of the same parents, which the MFMA block
+    // loads anyway (the fused kernel's operand order)
+    const float th = seed_theta_mfma_split(a.seed, wrows, stok, nb, lval, vt,
+                                           red, tid, a.seed.upack,
+                                           q * a.Fn + b0);
     if (tid < nb) a.nxt.theta[q * a.Fn + b0 + tid] = th;
     __syncthreads();  // stok and red are rewritten by the next block
-  }
-  // packed U rows of the next depth's parents (the fused kernel's operand
-  // order)
-  const uint4* Ug = reinterpret_cast<const uint4*>(a.seed.U);
-  const int cr = a.seed.r / 8;
-  for (int i = tid; i < a.Fn * cr; i += NT) {
-    const int jn = i / cr, c = i % cr;
-    const int tok = min(max(key_tok(ckey[bcand[jn]]), 0), a.seed.V - 1);
-    a.seed.upack[upack_index(q * a.Fn + jn, c, cr / 2)] =
-        Ug[(int64_t)tok * cr + c];
   }
 }
 
