@@ -119,6 +119,28 @@ K1Plan plan_k1(int P, int V, int r, int k, int uw_dtype, bool has_uw,
   if (r_ok) {
     pl.kind = K1_MFMA;
     pl.R16 = R16;
+    // At most 32 parents: the thin form, whose eight waves each take their
+    // own 32-row pieces of a slice (its LDS holds only the lists).  Slices
+    // of whole pieces, one per compute unit.
+    const size_t thin_lists = (size_t)kThinWaves * 64 * k * sizeof(ZV);
+    if (P <= 32 && thin_lists + 4096 <= kLdsPerCU) {
+      pl.thin = 1;
+      pl.NB = 1;
+      pl.NW = kThinWaves;
+      pl.lslots = 0;
+      pl.lds = thin_lists;
+      pl.lds_total = thin_lists + 2048;
+      const int pieces = (V + 31) / 32;
+      const int S = std::min(kCUs, pieces);
+      pl.vslice = (pieces + S - 1) / S * 32;
+      pl.n_slices = (V + pl.vslice - 1) / pl.vslice;
+      pl.n_tiles = (V + 63) / 64;
+      pl.tiles_per_slice = 0;
+      pl.cap = pl.n_slices * kThinWaves * 2 * k;
+      pl.grid = dim3(pl.n_slices, 1);
+      pl.block = dim3(kThinWaves * 64);
+      return pl;
+    }
     // static LDS: two W tiles and two L row buffers; dynamic: the lists
     const size_t wbytes = (size_t)2 * 64 * (2 * R16 + 1) * 16;  // padded rows
     auto slots_of = [&](int nb, int nw) {
@@ -232,8 +254,8 @@ hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s) {
 
 hipError_t launch_k1(const K1Plan& pl, const K1Args& a, hipStream_t s) {
   if (pl.kind == K1_MFMA) {
-    const bool st = a.group_fp > 0 && a.lslots > 0 && a.vec_ok &&
-                    a.L != nullptr && a.plrow == nullptr;
+    const bool st = !pl.thin && a.group_fp > 0 && a.lslots > 0 &&
+                    a.vec_ok && a.L != nullptr && a.plrow == nullptr;
     switch (pl.R16) {
       case 2: return st ? launch_mfma_r2s(pl, a, s) : launch_mfma_r2d(pl, a, s);
       case 4: return st ? launch_mfma_r4s(pl, a, s) : launch_mfma_r4d(pl, a, s);

@@ -488,6 +488,189 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
   }
 }
 
+// Thin form for frontiers of at most 32 parents (one parent block), where
+// the tiled kernel has a single wave with parents and the launch is bound by
+// streaming W one tile ahead.  Every wave of the workgroup takes its own
+// 32-row pieces of the slice (pieces wave, wave + 8, ...), loads their W
+// rows from global memory straight into MFMA operand registers (no LDS
+// staging, no barrier in the loop), and runs the same epilogue on its 16
+// rows per lane; the waves' (max, sum) partials meet in LDS at the end, and
+// every lane flushes its own top-k list.
+constexpr int kThinWaves = 8;
+
+template <int R16>
+__global__ __launch_bounds__(kThinWaves * 64) void markov_topk_thin(
+    K1Args a) {
+  constexpr int CH = 2 * R16;  // 16-byte chunks per W row
+  extern __shared__ __align__(16) unsigned char smem[];
+  ZV* lists = reinterpret_cast<ZV*>(smem);
+  __shared__ float2 wpart[kThinWaves][32];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, col = lane & 31;
+  const int slice = blockIdx.x;
+  const int r0 = slice * a.vslice, r1 = min(r0 + a.vslice, a.V);
+  const bool has_L = a.L != nullptr;
+  const int p = col;
+  const bool valid = p < a.P;
+  const int pc = valid ? p : a.P - 1;
+  float thr = valid ? (a.theta ? a.theta[p] : neg_inf()) : pos_inf();
+  int64_t row = a.plrow ? a.plrow[pc]
+                        : (int64_t)(a.group_fp > 0 ? pc / a.group_fp : pc) *
+                                  a.lrow_mul +
+                              a.lrow_add;
+  row = row < 0 ? 0 : (row >= a.L_rows ? a.L_rows - 1 : row);
+  const float* lrow = has_L ? a.L + row * a.lstride : nullptr;
+  bf16x8 uf[R16];
+  if (a.upack != nullptr) {
+    const uint4* up = a.upack + lane;  // block 0, one 1 KB load per step
+#pragma unroll
+    for (int kk = 0; kk < R16; ++kk)
+      uf[kk] = __builtin_bit_cast(bf16x8, up[kk * 64]);
+  } else {
+    const int ptk = min(max(a.ptok[pc], 0), a.V - 1);
+    const uint4* up = reinterpret_cast<const uint4*>(a.U) + (int64_t)ptk * CH + h;
+#pragma unroll
+    for (int kk = 0; kk < R16; ++kk)
+      uf[kk] = __builtin_bit_cast(bf16x8, up[2 * kk]);
+  }
+  if (!valid) {
+#pragma unroll
+    for (int kk = 0; kk < R16; ++kk)
+      uf[kk] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+  }
+  ZV* lst = lists + (wave * 64 + lane) * a.k;
+  int cnt = 0;
+  float cm2 = neg_inf(), ss = 0.f;
+  const uint4* Wg = reinterpret_cast<const uint4*>(a.W);
+  for (int v0 = r0 + 32 * wave; v0 < r1; v0 += 32 * kThinWaves) {
+    // W rows v0 + col (rows past V read row V - 1; their outputs are
+    // masked), chunks 2kk + h: the MFMA operand of rank step kk
+    const uint4* wp = Wg + (int64_t)min(v0 + col, a.V - 1) * CH + h;
+    bf16x8 wf[R16];
+#pragma unroll
+    for (int kk = 0; kk < R16; ++kk)
+      wf[kk] = __builtin_bit_cast(bf16x8, wp[2 * kk]);
+    // register j of this lane holds vocab vb + 8*(j/4) + j%4
+    const int vb = v0 + 4 * h;
+    const bool full = v0 + 32 <= a.V;
+    float4 lq[4];
+    if (has_L && full && a.vec_ok) {
+      // non-temporal: read once, while W is read again by the next depth
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 y = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(lrow + vb + 8 * g));
+        lq[g] = make_float4(y.x, y.y, y.z, y.w);
+      }
+    }
+    f32x16 acc;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < R16; ++kk)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[kk], uf[kk], acc, 0,
+                                                    0, 0);
+    float z[16];
+    if (full && a.vec_ok) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 l4 = has_L ? lq[g] : make_float4(0.f, 0.f, 0.f, 0.f);
+        z[4 * g + 0] = l4.x + acc[4 * g + 0];
+        z[4 * g + 1] = l4.y + acc[4 * g + 1];
+        z[4 * g + 2] = l4.z + acc[4 * g + 2];
+        z[4 * g + 3] = l4.w + acc[4 * g + 3];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int v = vb + 8 * (j >> 2) + (j & 3);
+        const float l = (has_L && v < a.V) ? lrow[v] : 0.f;
+        z[j] = v < a.V ? l + acc[j] : neg_inf();
+      }
+    }
+    float m = z[0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) m = fmaxf(m, z[j]);
+    if (a.z_out != nullptr && valid) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int v = vb + 8 * (j >> 2) + (j & 3);
+        if (v < a.V) a.z_out[(int64_t)p * a.V + v] = z[j];
+      }
+    }
+    // online log-sum-exp in log2 units
+    const float m2 = m * kLog2e;
+    if (m2 > cm2) {
+      ss *= __builtin_amdgcn_exp2f(cm2 - m2);
+      cm2 = m2;
+    }
+    if (m != neg_inf()) {
+      float sg[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(z[4 * g], kLog2e, -cm2));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(z[4 * g + 1], kLog2e, -cm2));
+        const float e2 = __builtin_amdgcn_exp2f(fmaf(z[4 * g + 2], kLog2e, -cm2));
+        const float e3 = __builtin_amdgcn_exp2f(fmaf(z[4 * g + 3], kLog2e, -cm2));
+        sg[g] = (e0 + e1) + (e2 + e3);
+      }
+      ss += (sg[0] + sg[1]) + (sg[2] + sg[3]);
+    }
+    // rare path, in vocabulary order (the list's tie rule needs it)
+    if (m >= thr) {
+      int v = vb;
+      int jend = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) jend = z[i] >= thr ? i + 1 : jend;
+#pragma unroll 1
+      for (int j = 0; j < jend; ++j) {
+        const float zj = z[0];
+#pragma unroll
+        for (int i = 0; i < 15; ++i) z[i] = z[i + 1];
+        if (zj >= thr && v < a.V) list_insert(lst, a.k, cnt, thr, zj, v);
+        v += ((j & 3) == 3) ? 5 : 1;
+      }
+    }
+  }
+  // partials: the two halves of the wave, then the waves
+  combine_halves(cm2, ss, lane);
+  if (h == 0) wpart[wave][col] = make_float2(cm2, ss);
+  __syncthreads();
+  if (wave == 0 && h == 0 && valid) {
+    float c = neg_inf();
+#pragma unroll
+    for (int w = 0; w < kThinWaves; ++w) c = fmaxf(c, wpart[w][col].x);
+    float s = 0.f;
+    if (c != neg_inf()) {
+#pragma unroll
+      for (int w = 0; w < kThinWaves; ++w) {
+        const float2 e = wpart[w][col];
+        if (e.x != neg_inf()) s += e.y * __builtin_amdgcn_exp2f(e.x - c);
+      }
+    }
+    a.part_c[(int64_t)slice * a.P + p] = c;
+    a.part_s[(int64_t)slice * a.P + p] = s;
+  }
+  if (valid && cnt > 0) {
+    const int pos = atomicAdd(&a.gcnt[p], cnt);
+    float* gz = a.gz + (int64_t)p * a.cap + pos;
+    int32_t* gv = a.gv + (int64_t)p * a.cap + pos;
+    for (int i = 0; i < cnt; ++i) {
+      gz[i] = lst[i].z;
+      gv[i] = lst[i].v;
+    }
+  }
+}
+
+template <int R16>
+hipError_t go_thin(const K1Plan& pl, const K1Args& a, hipStream_t s) {
+  auto fn = markov_topk_thin<R16>;
+  hipError_t e = allow_lds(reinterpret_cast<const void*>(fn), pl.lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fn, pl.grid, pl.block, pl.lds, s, a);
+  return hipGetLastError();
+}
+
 template <int NB, int NW, int R16, bool STAGED>
 hipError_t go_mfma(const K1Plan& pl, const K1Args& a, hipStream_t s) {
   auto fn = markov_topk_mfma<NB, NW, R16, STAGED>;
@@ -502,6 +685,9 @@ hipError_t go_mfma(const K1Plan& pl, const K1Args& a, hipStream_t s) {
 template <int R16, bool STAGED>
 hipError_t launch_mfma_rank(const K1Plan& pl, const K1Args& a,
                             hipStream_t s) {
+  if constexpr (!STAGED) {
+    if (pl.thin) return go_thin<R16>(pl, a, s);
+  }
   if (pl.NB == 1)
     return pl.NW == 8 ? go_mfma<1, 8, R16, STAGED>(pl, a, s)
                       : go_mfma<1, 1, R16, STAGED>(pl, a, s);

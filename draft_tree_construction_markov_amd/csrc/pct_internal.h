@@ -52,6 +52,7 @@ enum K1Kind { K1_MFMA = 0, K1_SIMPLE = 1 };
 
 struct K1Plan {
   int kind;
+  int thin;  // MFMA, at most 32 parents: markov_topk_thin (vslice rows)
   int NB, NW, R16;
   int lslots;  // LDS row slots for grouped rows (0: rows read directly)
   int n_tiles, tiles_per_slice, n_slices, vslice;
