@@ -120,6 +120,40 @@ def test_long_lists_across_ranks_and_parent_counts(r, k, P):
     assert near <= 2
 
 
+@pytest.mark.parametrize("V,r,P,k", [(2003, 128, 17, 12), (3000, 256, 32, 30),
+                                     (640, 32, 1, 4)])
+def test_thin_form_small_frontiers(V, r, P, k):
+    # at most 32 parents take the thin form (every wave its own 32-row
+    # pieces): a ragged last piece with V % 4 != 0 (scalar L reads), a full
+    # block of 32 parents with long lists, a single parent; the logits it
+    # writes, the log-normalisers and the top-k against the oracle
+    announce("markov thin", V, r, P, k)
+    U, W = synth.markov_factors(41 + r, V, r, True)
+    rows = 4
+    L = synth.drafter_logits(41, 1, rows, V, 3.0, (0.5, 2.0))[0]
+    rng = np.random.default_rng(V + P)
+    toks = rng.integers(0, V, size=P).astype(np.int32)
+    lrow = rng.integers(0, rows, size=P).astype(np.int32)
+    dU, dW = dev_factors(U, W)
+    lse, tt, tl, z = pct.markov_logits(dev_f32(L), dU, dW, dev_i32(toks),
+                                       dev_i32(lrow), k, want_z=True)
+    lse, tt, tl, z = (x.cpu().numpy() for x in (lse, tt, tl, z))
+    near = 0
+    for p in range(P):
+        M = oracle.markov_row(U, W, int(toks[p]))
+        ref = L[lrow[p]].astype(np.float64) + M
+        assert np.abs(z[p] - ref).max() <= 1e-5 * np.abs(ref).max()
+        ol, ot, oz, gap = oracle.row_stats(L[lrow[p]], M, k)
+        assert abs(lse[p] - ol) <= 1e-5 * max(1.0, abs(ol))
+        if np.array_equal(tt[p], ot):
+            olp = (oz - np.float32(ol)).astype(np.float32)
+            assert np.abs(tl[p] - olp).max() <= 1e-4
+        else:
+            assert gap < 1e-5, (p, tt[p], ot)
+            near += 1
+    assert near <= 1
+
+
 def test_invalid_arguments_rejected():
     announce("markov invalid args")
     t = dev_i32(np.zeros(4, np.int32))
