@@ -29,7 +29,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // streaming); each thread keeps its best element of the piece and the piece
 // contributes the kSeedT / kRowTopPieces best of those.  Any subset is a
 // valid seed; this one is close to the row's top kSeedT.
-constexpr int kRowTopPieces = 4;
+constexpr int kRowTopPieces = 8;
 constexpr int kRowTopSlots = kSeedT / kRowTopPieces;
 
 __global__ __launch_bounds__(256) void row_top_kernel(const float* L, int V,
