@@ -11,7 +11,6 @@
 
 namespace pct {
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 
 // ---------------------------------------------------------------------
@@ -549,62 +548,6 @@ __global__ __launch_bounds__(kInitThreads) void init_kernel(
   }
 }
 
-// Seed threshold of one parent (one wave) from LDS operands: the W rows
-// of the kSeedT seed tokens (wrows, r/8 + 1 16-byte chunks per row),
-// their logits lval and tokens vt (-1 = none), and the parent's U row (urow,
-// r/8 chunks).  Lane l takes seed token l%32 and half l/32 of the rank
-// dimension; the fp32 dot products differ from the fused kernel's MFMA sums
-// of the same exact products by less than the margin.  scratch: kSeedT
-// floats of LDS private to the wave.
-__device__ float seed_theta_lds(const SeedArgs& sa, const uint4* wrows,
-                                const uint4* urow, const float* lval,
-                                const int* vt, int lane, float* scratch) {
-  const int t = lane & 31, h = lane >> 5;
-  const int half = sa.r / 16;  // chunks per half of the rank dimension
-  const int cs = sa.r / 8 + 1;  // W row stride in chunks (one pad chunk)
-  // four independent partial sums keep the dependent chains short; each
-  // step is a two-product bf16 dot (at most one fp32 rounding per two exact
-  // products, inside the margin below), on the values and on their
-  // magnitudes (sign bits cleared)
-  float acc[4] = {0.f, 0.f, 0.f, 0.f}, aa[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int c = h * half; c < (h + 1) * half; ++c) {
-    const uint4 a4 = urow[c], b4 = wrows[t * cs + c];
-    const uint32_t ua[4] = {a4.x, a4.y, a4.z, a4.w};
-    const uint32_t wb[4] = {b4.x, b4.y, b4.z, b4.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[i] = __builtin_amdgcn_fdot2_f32_bf16(
-          __builtin_bit_cast(bf16x2, ua[i]), __builtin_bit_cast(bf16x2, wb[i]),
-          acc[i], false);
-      aa[i] = __builtin_amdgcn_fdot2_f32_bf16(
-          __builtin_bit_cast(bf16x2, ua[i] & 0x7fff7fffu),
-          __builtin_bit_cast(bf16x2, wb[i] & 0x7fff7fffu), aa[i], false);
-    }
-  }
-  const float m4 = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-  const float a4s = (aa[0] + aa[1]) + (aa[2] + aa[3]);
-  const float m = m4 + swap_halves(m4, lane);
-  const float A = a4s + swap_halves(a4s, lane);
-  const bool ok = h == 0 && vt[t] >= 0;
-  const float z = ok ? lval[t] + m : neg_inf();
-  const float Amax = wave_max(ok ? A : 0.f);
-  const float zmax = wave_max(ok ? fabsf(z) : 0.f);
-  // the k-th largest z: the value whose rank (ties by seed slot) is k-1
-  if (h == 0) scratch[t] = z;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  int rank = 0;
-  for (int o = 0; o < kSeedT; ++o) {
-    const float zo = scratch[o];
-    rank += zo > z || (zo == z && o < t);
-  }
-  const float kth = wave_max(h == 0 && rank == sa.k - 1 ? z : neg_inf());
-  const float margin = 4.f * (float)sa.r * 5.9604645e-8f * Amax +
-                       4.f * 1.1920929e-7f * zmax + 1e-30f;
-  return kth - margin;
-}
-
 // The log-normaliser of one parent from its (c, s) partials, one wave:
 // part(i) returns partial i of S.  Each lane keeps a running (max, sum) with
 // a double sum; lanes combine by DPP reductions.
@@ -632,15 +575,20 @@ __device__ float wave_lse_from(F&& part, int S, int lane) {
 // One workgroup per request: children of every frontier parent, their
 // scores and pool keys, the beam of the next depth and its seeds.
 //  1. all independent loads first: the next row's seed tokens, their logits
-//     and W rows; the partials of up to 16 parents, read coalesced ([S][P]
+//     and W rows; the partials of up to 8 parents, read coalesced ([S][P]
 //     rows of consecutive parents) into LDS;
 //  2. one wave per parent: log-normaliser and top-k of its candidates;
-//  3. the U rows of every child are prefetched to LDS (direct global->LDS
-//     loads) while the beam (rank of each child's key) is computed;
-//  4. one wave per new parent: its seed threshold for the next depth.
-constexpr int kExpandWaves = 16;
+//  3. the beam (rank of each child's key);
+//  4. the new parents' seed thresholds for the next depth as one MFMA block
+//     per 32 of them (their U rows pass through its operand registers into
+//     the packed rows of the next depth), or one wave per new parent when
+//     the seeds cannot use MFMA.
+// Eight waves: the MFMA seed block needs more than the 128 registers a
+// 1024-thread workgroup allows; the single kernel serves frontiers below 64
+// parents in all (batch-1 builds, depth 1), at most 8 parents per request
+// in the benchmark's workloads.
+constexpr int kExpandWaves = 8;
 constexpr int kStageSlices = 256;  // partials per parent staged in LDS
-constexpr int kUPre = 128;         // children whose U rows are prefetched
 __global__ __launch_bounds__(kExpandWaves * 64) void expand_kernel(
     ExpandArgs a) {
   __shared__ uint64_t ckey[kMaxCand];
@@ -653,7 +601,7 @@ __global__ __launch_bounds__(kExpandWaves * 64) void expand_kernel(
   static_assert(sizeof(pst) >= (kMaxCand + kExpandWaves * kSeedT) * 4,
                 "beam indices and seed scratch");
   __shared__ uint4 wrows[kSeedT * kSeedRowChunks];
-  __shared__ uint4 upre[kUPre * 32];  // U rows (r <= 256: 32 chunks each)
+  __shared__ float red[3 * 32 * 64];  // the seed block's partial sums
   __shared__ float lval[kSeedT];
   __shared__ int vt[kSeedT];
   constexpr int NT = kExpandWaves * 64;
@@ -662,13 +610,8 @@ __global__ __launch_bounds__(kExpandWaves * 64) void expand_kernel(
   const int NC = a.Fp * a.k;
   const int row = q * a.B + a.d;  // L row of depth d+1
   const bool lseed = a.d < a.B && seed_by_mfma(a.seed);  // bf16, r <= 256
-  const int ch = a.seed.r / 8;
   const bool staged = !a.shared_stats && a.n_slices <= kStageSlices;
-  const bool upref = lseed && NC <= kUPre;
-  // each wave prefetches its parent's children when they fill whole
-  // 64-chunk instructions
-  const bool upwave = upref && (a.k * ch) % 64 == 0;
-  // partials of a group of up to 16 parents into LDS; the first group's
+  // partials of a group of up to 8 parents into LDS; the first group's
   // loads are issued before the seed staging so that the two overlap
   constexpr int kStageIt = kExpandWaves * kStageSlices / NT;
   float2 pre[kStageIt];
@@ -756,44 +699,10 @@ __global__ __launch_bounds__(kExpandWaves * 64) void expand_kernel(
                        ctok[c] = v;
                        a.pool_key[(int64_t)q * a.pool_n + pid] = key;
                      }, g0 == 0, hz, hv);
-      if (upwave) {
-        // this parent's children's U rows, issued as soon as their tokens
-        // are known (direct global->LDS loads, 64 chunks per instruction)
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const uint4* Ug = reinterpret_cast<const uint4*>(a.seed.U);
-        const int base = j * a.k * ch;
-        for (int i0 = 0; i0 < a.k * ch; i0 += 64) {
-          const int i = i0 + lane;
-          const int c = j * a.k + i / ch, cc = i % ch;
-          const int tok = min(max(ctok[c], 0), a.seed.V - 1);
-          __builtin_amdgcn_global_load_lds(
-              (const __attribute__((address_space(1))) void*)(
-                  Ug + (int64_t)tok * ch + cc),
-              (__attribute__((address_space(3))) void*)(upre + base + i0), 16,
-              0, 0);
-        }
-      }
     }
   }
   __syncthreads();
 
-  // U rows of every child, in flight while the beam is ranked (when the
-  // waves did not issue their own children's rows above)
-  if (upref && !upwave) {
-    const uint4* Ug = reinterpret_cast<const uint4*>(a.seed.U);
-    for (int i0 = wave * 64; i0 < NC * ch; i0 += NT) {
-      const int i = min(i0 + lane, NC * ch - 1);
-      const int c = i / ch, cc = i % ch;
-      const int tok = min(max(ctok[c], 0), a.seed.V - 1);
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(Ug +
-                                                          (int64_t)tok * ch +
-                                                          cc),
-          (__attribute__((address_space(3))) void*)(upre + i0), 16, 0, 0);
-    }
-  }
   // beam: the Fn smallest keys of this depth's children (keys are distinct:
   // (parent, token) pairs are unique); rank counts split over the threads
   const int parts = NC <= NT ? max(1, NT / NC) : 1;
@@ -830,41 +739,38 @@ __global__ __launch_bounds__(kExpandWaves * 64) void expand_kernel(
     }
   }
   if (a.d >= a.B) return;
-  if (upref) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  // seeds of the next depth's parents, one wave each
-  for (int i = wave; i < a.Fn; i += kExpandWaves) {
-    float th;
-    if (lseed) {
-      const int c = bcand[i];
-      const uint4* urow;
-      if (upref) {
-        urow = upre + c * ch;
-      } else {
-        urow = reinterpret_cast<const uint4*>(a.seed.U) +
-               (int64_t)min(max(ctok[c], 0), a.seed.V - 1) * ch;
-      }
-      // wave scratch after the beam indices (kMaxCand ints) in pst
-      float* scr = reinterpret_cast<float*>(pst) + kMaxCand + wave * kSeedT;
-      th = seed_theta_lds(a.seed, wrows, urow, lval, vt, lane, scr);
-    } else {
-      th = seed_theta(a.seed, ctok[bcand[i]], row, lane);
+  if (lseed) {
+    // the new parents' tokens in rank order (the ranks are consumed)
+    int32_t* stok = crank;
+    for (int i = tid; i < a.Fn; i += NT) stok[i] = ctok[bcand[i]];
+    __syncthreads();
+    for (int b0 = 0; b0 < a.Fn; b0 += 32) {
+      const int nb = min(32, a.Fn - b0);
+      const float th = seed_theta_mfma_split(a.seed, wrows, stok + b0, nb,
+                                             lval, vt, red, tid, a.seed.upack,
+                                             q * a.Fn + b0);
+      if (tid < nb) a.nxt.theta[q * a.Fn + b0 + tid] = th;
+      __syncthreads();  // red is rewritten by the next block
     }
+    return;
+  }
+  // seeds without MFMA, one wave per new parent
+  for (int i = wave; i < a.Fn; i += kExpandWaves) {
+    const float th = seed_theta(a.seed, ctok[bcand[i]], row, lane);
     if (lane == 0) a.nxt.theta[q * a.Fn + i] = th;
   }
   // packed U rows of the next depth's parents (the fused kernel's operand
-  // order), from the prefetched rows when there are any
+  // order)
   if (a.seed.upack != nullptr) {
     const uint4* Ug = reinterpret_cast<const uint4*>(a.seed.U);
     const int cr = a.seed.r / 8;
     for (int i = tid; i < a.Fn * cr; i += NT) {
       const int j = i / cr, c = i % cr;
-      const int cb = bcand[j];
-      const uint4 v =
-          upref ? upre[cb * cr + c]
-                : Ug[(int64_t)min(max(ctok[cb], 0), a.seed.V - 1) * cr + c];
-      a.seed.upack[upack_index(q * a.Fn + j, c, cr / 2)] = v;
+      const int tok = min(max(ctok[bcand[j]], 0), a.seed.V - 1);
+      a.seed.upack[upack_index(q * a.Fn + j, c, cr / 2)] =
+          Ug[(int64_t)tok * cr + c];
     }
   }
 }
