@@ -218,8 +218,12 @@ def classify(g, o, q, ctx):
     """('exact' | 'near', detail); raises AssertionError for FAIL."""
     if _same_tree(g, o, q):
         n = int(o["n_nodes"][q])
-        d = np.abs(g["score"][q][:n].astype(np.float64) -
-                   o["score"][q][:n].astype(np.float64))
+        gs = g["score"][q][:n].astype(np.float64)
+        os_ = o["score"][q][:n].astype(np.float64)
+        # equal scores (-inf included: children of rows with fewer finite
+        # logits than k) differ by nothing
+        with np.errstate(invalid="ignore"):
+            d = np.where(gs == os_, 0.0, np.abs(gs - os_))
         md = float(d.max()) if n else 0.0
         assert md <= SCORE_TOL, (q, f"score diff {md}")
         return "exact", md

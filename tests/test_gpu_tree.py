@@ -133,6 +133,26 @@ def test_two_kernel_expand_shapes(batch, B, V, k, beam, N, r):
     assert bins["near"] <= max(1, batch // 16), bins
 
 
+@pytest.mark.parametrize("N", [12, 200, 248])
+def test_rows_with_few_finite_logits(N):
+    # three finite logits per row, k = 8: most children score -inf, so their
+    # keys share the score bits and differ in parent and token only; the
+    # top-N cut falls among them (N = 200 of a 248-child pool) or keeps the
+    # whole pool
+    L, U, W, A = _random(5, 3, 4, 600, 32)
+    rng = np.random.default_rng(1)
+    for q in range(3):
+        for d in range(4):
+            keep = rng.choice(600, 3, replace=False)
+            row = np.full(600, -np.inf, np.float32)
+            row[keep] = L[q, d, keep]
+            L[q, d] = row
+    g, o, bins = run_and_compare(L, U, W, A, 8, 10, N)
+    assert bins["exact"] == 3, bins
+    if N == 200:
+        assert np.isneginf(g["score"][0]).sum() > 100
+
+
 @pytest.mark.parametrize("batch,B,V,k,beam,N,r", [
     # the global top-N selects the N smallest keys of a pool by radix
     # select, then sorts them (runs of 64 by counting, merged level by
