@@ -59,6 +59,7 @@ struct TreePlan {
   int max_slices_P;
   int max_cap_P;
   int max_P;
+  int max_tq;  // tile-queue counters of the largest fused launch
 };
 
 pct_status plan_tree(const pct_tree_shape* sh, TreePlan& tp) {
@@ -89,6 +90,7 @@ pct_status plan_tree(const pct_tree_shape* sh, TreePlan& tp) {
   tp.max_slices_P = 0;
   tp.max_cap_P = 0;
   tp.max_P = 0;
+  tp.max_tq = 0;
   for (int d = 1; d <= B; ++d) {
     // without Markov factors every parent of a request shares its row
     const int P = has_uw ? sh->batch * tp.F[d - 1] : sh->batch;
@@ -96,6 +98,7 @@ pct_status plan_tree(const pct_tree_shape* sh, TreePlan& tp) {
                        has_uw ? tp.F[d - 1] : 0);
     const int sp = tp.k1[d].n_slices * P;
     const int cp = tp.k1[d].cap * P;
+    if (tp.k1[d].n_tq > tp.max_tq) tp.max_tq = tp.k1[d].n_tq;
     if (sp > tp.max_slices_P) tp.max_slices_P = sp;
     if (cp > tp.max_cap_P) tp.max_cap_P = cp;
     if (P > tp.max_P) tp.max_P = P;
@@ -114,6 +117,7 @@ struct TreeWs {
   uint64_t* pool_key;
   uint4* upack;  // packed U rows of one depth's parents (MFMA plans only)
   uint64_t* ckey;  // one depth's child keys (split expand)
+  int32_t* tq;     // fused-kernel tile queue (cleared by init)
 };
 
 size_t carve_tree(const pct_tree_shape* sh, const TreePlan& tp, void* ws,
@@ -140,6 +144,7 @@ size_t carve_tree(const pct_tree_shape* sh, const TreePlan& tp, void* ws,
                                      (sh->r / 8)
                                : 0);
   w.ckey = c.take<uint64_t>((size_t)FB * sh->k);
+  w.tq = c.take<int32_t>(tp.max_tq);
   return c.off;
 }
 
@@ -199,7 +204,7 @@ size_t pct_markov_logits_workspace(int32_t P, int32_t V, int32_t k) {
     Carve c{nullptr};
     c.take<float>((size_t)pl->n_slices * P);
     c.take<float>((size_t)pl->n_slices * P);
-    c.take<int32_t>(P);
+    c.take<int32_t>(P + pl->n_tq);
     c.take<float>((size_t)pl->cap * P);
     c.take<int32_t>((size_t)pl->cap * P);
     if (c.off > need) need = c.off;
@@ -242,7 +247,10 @@ pct_status pct_markov_logits(const float* L, int64_t L_row_stride,
   K1Args a{};
   a.part_c = c.take<float>((size_t)pl.n_slices * P);
   a.part_s = c.take<float>((size_t)pl.n_slices * P);
-  a.gcnt = c.take<int32_t>(P);
+  // the candidate counters, then the tile queue: one clear for both
+  a.gcnt = c.take<int32_t>(P + pl.n_tq);
+  a.tq = pl.n_tq > 0 ? a.gcnt + P : nullptr;
+  a.tiles_per_slice = pl.tiles_per_slice;
   a.gz = c.take<float>((size_t)pl.cap * P);
   a.gv = c.take<int32_t>((size_t)pl.cap * P);
   a.L = L;
@@ -259,13 +267,12 @@ pct_status pct_markov_logits(const float* L, int64_t L_row_stride,
   a.ptok = parent_tok;
   a.plrow = L ? parent_Lrow : nullptr;
   a.theta = nullptr;
-  a.tiles_per_slice = pl.tiles_per_slice;
   a.n_tiles = pl.n_tiles;
   a.n_slices = pl.n_slices;
   a.vslice = pl.vslice;
   a.cap = pl.cap;
   a.z_out = z_out;
-  hipError_t e = launch_fill_i32(a.gcnt, P, 0, s);
+  hipError_t e = launch_fill_i32(a.gcnt, P + pl.n_tq, 0, s);
   if (e != hipSuccess) return hip_fail(e, "clear counters");
   {
     ProfScope ps(PROF_MARKOV, P, s);
@@ -353,7 +360,7 @@ pct_status pct_build_tree(const pct_tree_shape* shape, const float* L,
   Frontier f1{w.ftok[1], w.fpid[1], w.flrow[1], w.fs[1], w.ftheta[1]};
   {
     ProfScope ps(PROF_INIT, batch, s);
-    e = launch_init(batch, B, anchor, f0, w.gcnt[1], sa, s);
+    e = launch_init(batch, B, anchor, f0, w.gcnt[1], w.tq, tp.max_tq, sa, s);
   }
   if (e != hipSuccess) return hip_fail(e, "init kernel");
 
@@ -393,8 +400,7 @@ pct_status pct_build_tree(const pct_tree_shape* shape, const float* L,
       a.lrow_add = d - 1;
       a.theta = nullptr;
     }
-    a.tiles_per_slice = pl.tiles_per_slice;
-    a.n_tiles = pl.n_tiles;
+      a.n_tiles = pl.n_tiles;
     a.n_slices = pl.n_slices;
     a.vslice = pl.vslice;
     a.part_c = w.part_c;
@@ -405,6 +411,8 @@ pct_status pct_build_tree(const pct_tree_shape* shape, const float* L,
     a.cap = pl.cap;
     a.z_out = nullptr;
     a.upack = sa.upack;
+    a.tq = pl.n_tq > 0 ? w.tq : nullptr;
+    a.tiles_per_slice = pl.tiles_per_slice;
     {
       ProfScope ps(PROF_MARKOV, P, s);
       e = launch_k1(pl, a, s);

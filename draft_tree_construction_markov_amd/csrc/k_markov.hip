@@ -135,7 +135,6 @@ K1Plan plan_k1(int P, int V, int r, int k, int uw_dtype, bool has_uw,
       pl.vslice = (pieces + S - 1) / S * 32;
       pl.n_slices = (V + pl.vslice - 1) / pl.vslice;
       pl.n_tiles = (V + 63) / 64;
-      pl.tiles_per_slice = 0;
       pl.cap = pl.n_slices * kThinWaves * 2 * k;
       pl.grid = dim3(pl.n_slices, 1);
       pl.block = dim3(kThinWaves * 64);
@@ -196,12 +195,29 @@ K1Plan plan_k1(int P, int V, int r, int k, int uw_dtype, bool has_uw,
     if (per_cu > by_waves) per_cu = by_waves;
     const int PT = (P + 32 * pl.NB * pl.NW - 1) / (32 * pl.NB * pl.NW);
     pl.n_tiles = (V + 63) / 64;
-    int target = kCUs * per_cu;
-    int S = (target + PT - 1) / PT;
-    if (S > pl.n_tiles) S = pl.n_tiles;
-    if (S < 1) S = 1;
-    pl.tiles_per_slice = (pl.n_tiles + S - 1) / S;
-    pl.n_slices = (pl.n_tiles + pl.tiles_per_slice - 1) / pl.tiles_per_slice;
+    if (pl.NB == 2) {
+      // 64 parents per wave, where the tiles are bound by the MFMA chain
+      // and the epilogue: the workgroups of a parent tile take vocabulary
+      // tiles from a queue, so as many as the chip holds at once share the
+      // tiles and the fastest take the most (a slice is the set of tiles
+      // one workgroup took).  Measured at 512 parents: 48.1 -> 45.3 us.
+      int S = kCUs * per_cu / PT;
+      if (S > pl.n_tiles) S = pl.n_tiles;
+      if (S < 1) S = 1;
+      pl.n_slices = S;
+      pl.tiles_per_slice = 0;
+      pl.n_tq = 2 * PT;
+    } else {
+      // fewer parents per wave, where the tiles are bound by their loads:
+      // contiguous slices (the queued order measured 33.8 -> 39.4 us at 256
+      // parents)
+      int S = (kCUs * per_cu + PT - 1) / PT;
+      if (S > pl.n_tiles) S = pl.n_tiles;
+      if (S < 1) S = 1;
+      pl.tiles_per_slice = (pl.n_tiles + S - 1) / S;
+      pl.n_slices = (pl.n_tiles + pl.tiles_per_slice - 1) / pl.tiles_per_slice;
+      pl.n_tq = 0;
+    }
     pl.cap = pl.n_slices * 2 * k;
     pl.grid = dim3(pl.n_slices, PT);
     pl.block = dim3(pl.NW * 64);
@@ -254,6 +270,10 @@ hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s) {
 
 hipError_t launch_k1(const K1Plan& pl, const K1Args& a, hipStream_t s) {
   if (pl.kind == K1_MFMA) {
+    // the queued order is compiled into the kernels of two parent blocks
+    // per wave
+    if ((pl.NB == 2) != (pl.n_tq > 0) || (pl.n_tq > 0 && a.tq == nullptr))
+      return hipErrorInvalidValue;
     const bool st = !pl.thin && a.group_fp > 0 && a.lslots > 0 &&
                     a.vec_ok && a.L != nullptr && a.plrow == nullptr;
     switch (pl.R16) {

@@ -18,8 +18,11 @@
 // (NB=1) parents resident in registers for the whole kernel; the W tile is
 // staged through LDS by direct global->LDS loads (double-buffered,
 // XOR-swizzled 16-byte chunks) and shared by all waves of the workgroup;
-// so are the workgroup's L rows when parents are grouped by request.  A workgroup covers one slice of the
-// vocabulary for up to NB*NW*32 parents; slices x parent tiles form the grid.
+// so are the workgroup's L rows when parents are grouped by request.  A
+// workgroup covers a slice of the vocabulary for up to NB*NW*32 parents;
+// slices x parent tiles form the grid.  With 64 parents per wave a slice is
+// the set of 64-row tiles the workgroup took from a queue shared by the
+// workgroups of its parent tile; otherwise it is a contiguous run of tiles.
 #pragma once
 #include "pct_device.h"
 #include "pct_internal.h"
@@ -39,8 +42,10 @@ constexpr int wstride() {
   return 2 * R16 + 1;
 }
 
-// Insert z (vocab v) into a lane's top-k list.  Within one lane the vocab
-// index only grows, so an entry equal to the current minimum never wins.
+// Insert z (vocab v) into a lane's top-k list: the list keeps the k largest
+// elements offered, an equal logit ranking the smaller vocabulary index
+// first, whatever the order in which they come (a workgroup's tiles arrive
+// in queue order).
 __device__ __forceinline__ void list_insert(ZV* lst, int k, int& cnt,
                                             float& thr, float z, int v) {
   if (cnt < k) {
@@ -51,7 +56,7 @@ __device__ __forceinline__ void list_insert(ZV* lst, int k, int& cnt,
       for (int i = 1; i < k; ++i) mn = fminf(mn, lst[i].z);
       thr = mn;
     }
-  } else if (z > thr) {
+  } else if (z >= thr) {
     int wi = 0;
     float wz = lst[0].z;
     int wv = lst[0].v;
@@ -63,6 +68,7 @@ __device__ __forceinline__ void list_insert(ZV* lst, int k, int& cnt,
         wv = e.v;
       }
     }
+    if (z == wz && v > wv) return;
     lst[wi] = ZV{z, v};
     float mn = lst[0].z;
     for (int i = 1; i < k; ++i) mn = fminf(mn, lst[i].z);
@@ -138,8 +144,25 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, col = lane & 31;
   const int slice = blockIdx.x;
-  const int t0 = slice * a.tiles_per_slice;
-  const int t1 = min(t0 + a.tiles_per_slice, a.n_tiles);
+  const int nwg = gridDim.x;
+  // Tile order.  Without a queue, workgroup s takes the contiguous tiles
+  // t0 .. t1-1 of its slice.  With one (two counters per parent tile:
+  // tickets handed out, workgroups finished), its tiles 0 and 1 are s and
+  // s + nwg and tile i >= 2 is 2*nwg plus a ticket taken during tile i - 2,
+  // so the workgroups that run fastest take the most tiles; their ids pass
+  // through the ring sq[i % 4].  An id past the last tile ends the loop.
+  // (the shapes of 64 parents per wave use the queue; the planner gives
+  // their launches one)
+  constexpr bool queued = NB == 2;
+  int32_t* tq = queued ? a.tq + 2 * blockIdx.y : nullptr;
+  const int t0 = queued ? slice : slice * a.tiles_per_slice;
+  const int t1 =
+      queued ? a.n_tiles : min(t0 + a.tiles_per_slice, a.n_tiles);
+  auto fixed_id = [&](int i) __attribute__((always_inline)) {
+    const int t = queued ? slice + i * nwg : t0 + i;
+    return t < t1 ? t : a.n_tiles;
+  };
+  __shared__ int sq[4];
   const int p0 = blockIdx.y * SPAN;
   const int pw = p0 + wave * (NB * 32);
   const bool has_L = a.L != nullptr;
@@ -235,11 +258,14 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
                                        (lds_ptr_t)(wd + gi * 64), 16, 0, 0);
     }
     // L rows non-temporal (aux 2): each is read once per launch, while W
-    // is read again by every depth and should stay in the caches
+    // is read again by every depth and should stay in the caches.  The LDS
+    // destinations are per-wave values, derived from a scalar copy of the
+    // wave index so that none of them occupies a vector register.
     if (STAGED) {
+      const int ws = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
       for (int i = 0; i < LMAX; ++i) {
-        const int gi = wave + i * NW;
+        const int gi = ws + i * NW;
         if (gi * 64 < nslots * 16)
           __builtin_amdgcn_global_load_lds((gbl_ptr_t)lsrc[i],
                                            (lds_ptr_t)(ld + gi * 64), 16, 0,
@@ -389,9 +415,8 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
         }
         // rare path: some element may enter this lane's top-k.  A rolled
         // loop that shifts z keeps the code small; z is dead afterwards.
-        // Elements go to the list in vocabulary order (its tie rule needs
-        // it), and the loop ends after the last element at or above the
-        // threshold (which only rises as the list fills).
+        // The loop ends after the last element at or above the threshold
+        // (which only rises as the list fills).
         const bool hit = m >= thr[b];
         if (__any(hit)) {
           if (hit) {
@@ -427,18 +452,35 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
   //   late:  epi(t-1,1) | mma(t,0) epi(t,0) mma(t,1)
   // The barrier at "|" follows the late waves' last read of tile t-1's L
   // rows, so the loads of tile t+1 into that buffer are issued there; the
-  // barrier at the end of the tile waits for them.
+  // barrier at the end of the tile waits for them.  Tile i of the workgroup
+  // is tile id t (its predecessor tp, its successor tn).  During it one
+  // thread publishes the id of tile i + 2 at the end; with a queue it takes
+  // that tile's ticket just before the tile's loads, so the wait for those
+  // loads at the end of the tile also covers the atomic.
   const bool late = NW >= 2 && wave >= NW / 2;
   // a wave with no parents only loads its share of the tiles
   const bool active = pw < a.P;
-  auto tile = [&](int t, const uint4* wt, const float4* lt, uint4* wn,
-                  float4* ln, const float4* lp) __attribute__((always_inline)) {
+  const bool taker = tid == (NW >= 2 ? NW / 2 : 0) * 64;
+  auto take = [&](int which) __attribute__((always_inline)) {
+    // the counter's address as a per-lane value: a uniform address would
+    // let the compiler turn the atomic into a wave-wide one that it waits
+    // for at once
+    int off = which;
+    asm volatile("" : "+v"(off));
+    return __hip_atomic_fetch_add(tq + off, 1, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+  };
+  auto tile = [&](int i, int t, int tp, int tn, const uint4* wt,
+                  const float4* lt, uint4* wn, float4* ln,
+                  const float4* lp) __attribute__((always_inline)) {
     if (active) {
       if (!late) mma(wt, 0);
-      else if (t > t0) epi(t - 1, 1, lp);
+      else if (i > 0) epi(tp, 1, lp);
     }
     __syncthreads();
-    if (t + 1 < t1) issue(t + 1, wn, ln);
+    int ticket = 0;
+    if (taker && queued) ticket = take(0);
+    if (tn < a.n_tiles) issue(tn, wn, ln);
     if (!active) {
     } else if (!late) {
       epi(t, 0, lt);
@@ -450,9 +492,15 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
       mma(wt, 1);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // (a ticket can only be negative if the queue was not cleared: then the
+    // workgroup stops rather than read outside W)
+    if (taker && queued)
+      sq[(i + 2) & 3] = ticket >= 0 ? 2 * nwg + ticket : a.n_tiles;
     __syncthreads();
   };
-  if (t0 < t1) issue(t0, w0, l0);
+  int cur = fixed_id(0);
+  if (tid == 0 && queued) sq[1] = fixed_id(1);
+  if (cur < a.n_tiles) issue(cur, w0, l0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   // the fragments pass through an opaque statement here, so the compiler
   // neither predicates their loads on the zeroing below nor waits for them
@@ -469,12 +517,30 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
     }
   }
   __syncthreads();
-  for (int t = t0; t < t1; t += 2) {
-    tile(t, w0, l0, w1, l1, l1);
-    if (t + 1 < t1) tile(t + 1, w1, l1, w0, l0, l0);
+  int i = 0, prv = 0;
+  // the id of tile i + 1: from the ring with a queue, else computed
+  auto next_id = [&](int i) __attribute__((always_inline)) {
+    return queued ? __builtin_amdgcn_readfirstlane(sq[(i + 1) & 3])
+                  : fixed_id(i + 1);
+  };
+  while (cur < a.n_tiles) {
+    int nxt = next_id(i);
+    tile(i, cur, prv, nxt, w0, l0, w1, l1, l1);
+    prv = cur;
+    cur = nxt;
+    ++i;
+    if (cur >= a.n_tiles) break;
+    nxt = next_id(i);
+    tile(i, cur, prv, nxt, w1, l1, w0, l0, l0);
+    prv = cur;
+    cur = nxt;
+    ++i;
   }
-  if (active && late && t1 > t0)
-    epi(t1 - 1, 1, ((t1 - 1 - t0) & 1) ? l1 : l0);
+  // every ticket of this workgroup has returned: count the workgroup as
+  // finished (the answer is looked at after the flush)
+  int done = 0;
+  if (taker && queued) done = take(1);
+  if (active && late && i > 0) epi(prv, 1, ((i - 1) & 1) ? l1 : l0);
 
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
@@ -485,6 +551,11 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
       const int li = (wave * 64 + lane) * NB + b;
       flush_lane(a, p, slice, c2, s, lists + li * a.k, lcount[li], h == 0);
     }
+  }
+  // the last workgroup to finish clears the queue for the next launch
+  if (taker && queued && done == nwg - 1) {
+    __hip_atomic_store(&tq[0], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&tq[1], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

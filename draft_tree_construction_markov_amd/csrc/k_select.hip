@@ -479,7 +479,8 @@ __device__ float seed_theta_mfma_split(const SeedArgs& sa, const uint4* wrows,
 // first wave computes the threshold.
 constexpr int kInitThreads = 256;
 __global__ __launch_bounds__(kInitThreads) void init_kernel(
-    int B, const int32_t* anchor, Frontier f, int32_t* gcnt, SeedArgs sa) {
+    int B, const int32_t* anchor, Frontier f, int32_t* gcnt, int32_t* tq,
+    int n_tq, SeedArgs sa) {
   static_assert(kInitThreads == 256, "four waves (the split seed routine)");
   __shared__ uint4 wrows[kSeedT * kSeedRowChunks];
   __shared__ float red[3 * 32 * 64];
@@ -546,6 +547,10 @@ __global__ __launch_bounds__(kInitThreads) void init_kernel(
     f.theta[q] = th;
     gcnt[q] = 0;
   }
+  // the fused kernel's tile queue starts the build cleared (every launch
+  // leaves it cleared)
+  if (q == 0)
+    for (int i = tid; i < n_tq; i += kInitThreads) tq[i] = 0;
 }
 
 // The log-normaliser of one parent from its (c, s) partials, one wave:
@@ -1587,9 +1592,10 @@ hipError_t launch_rowtop(const float* L, int rows, int V, int64_t lstride,
 }
 
 hipError_t launch_init(int batch, int B, const int32_t* anchor, Frontier f,
-                       int32_t* gcnt, const SeedArgs& sa, hipStream_t s) {
+                       int32_t* gcnt, int32_t* tq, int n_tq,
+                       const SeedArgs& sa, hipStream_t s) {
   hipLaunchKernelGGL(init_kernel, dim3(batch), dim3(kInitThreads), 0, s, B,
-                     anchor, f, gcnt, sa);
+                     anchor, f, gcnt, tq, n_tq, sa);
   return hipGetLastError();
 }
 

@@ -33,7 +33,8 @@ struct K1Args {
   // (lslots row slots per buffer).
   int group_fp, lslots;
   const float* theta;    // [P] candidate threshold seeds (null: -inf)
-  int tiles_per_slice, n_tiles, n_slices;  // mfma: 64-vocab tiles
+  int n_tiles, n_slices;  // mfma: 64-vocab tiles; workgroups per parent tile
+  int tiles_per_slice;    // mfma without a tile queue: contiguous tiles each
   int vslice;                              // simple: vocab per slice
   float* part_c;   // [n_slices][P] running max in log2 units
   float* part_s;   // [n_slices][P] sum of 2^(z*log2e - part_c)
@@ -46,6 +47,11 @@ struct K1Args {
   // 16-byte chunk c of parent p's row at ((p/32) * r/16 + c/2) * 64 +
   // (c%2) * 32 + p%32
   const uint4* upack;
+  // Tile queue of the tiled MFMA kernel, two counters per parent tile
+  // (grid row): tickets handed out, workgroups finished.  Both are zero
+  // before a launch and the launch's last workgroup zeroes them again.
+  // Null: every workgroup takes its slice of contiguous tiles.
+  int32_t* tq;
 };
 
 enum K1Kind { K1_MFMA = 0, K1_SIMPLE = 1 };
@@ -56,6 +62,7 @@ struct K1Plan {
   int NB, NW, R16;
   int lslots;  // LDS row slots for grouped rows (0: rows read directly)
   int n_tiles, tiles_per_slice, n_slices, vslice;
+  int n_tq;  // tile-queue counters the launch needs (0: contiguous slices)
   int cap;  // candidate capacity per parent
   size_t lds;        // dynamic LDS bytes of the launch
   size_t lds_total;  // static + dynamic, for occupancy planning
@@ -175,7 +182,8 @@ struct TopNArgs {
 hipError_t launch_rowtop(const float* L, int rows, int V, int64_t lstride,
                          int vec_ok, int32_t* rowtop, hipStream_t s);
 hipError_t launch_init(int batch, int B, const int32_t* anchor, Frontier f,
-                       int32_t* gcnt, const SeedArgs& sa, hipStream_t s);
+                       int32_t* gcnt, int32_t* tq, int n_tq,
+                       const SeedArgs& sa, hipStream_t s);
 hipError_t launch_expand(const ExpandArgs& a, hipStream_t s);
 // the split form applies to bf16 factors with seeds by MFMA, staged
 // partials and one statistics row per parent
