@@ -202,6 +202,24 @@ def test_chain_and_uniform_ties():
     assert bins["exact"] == 2
 
 
+def test_integer_ties_in_queued_tile_order():
+    # Integer factors and logits: every z = L + U.W is an exact integer, so
+    # children of one parent tie exactly, also at the top-k boundary.  Depth
+    # 3 has 320 parents over V = 40000 (625 vocabulary tiles): the fused
+    # kernel hands the tiles past the first 512 out from its queue, so a
+    # lane meets its tiles out of vocabulary order.  The oracle keeps the
+    # smaller token of a tie; the GPU tree must match it exactly (a tie the
+    # kernel broke the other way would show as a near-tie bin).
+    rng = np.random.default_rng(29)
+    batch, B, V, r = 20, 3, 40000, 256
+    U = synth.bf16_bits(rng.integers(-1, 2, size=(V, r)).astype(np.float32))
+    W = synth.bf16_bits(rng.integers(-1, 2, size=(V, r)).astype(np.float32))
+    L = rng.integers(-4, 5, size=(batch, B, V)).astype(np.float32)
+    A = rng.integers(0, V, size=batch).astype(np.int32)
+    g, o, bins = run_and_compare(L, U, W, A, 8, 16, 64)
+    assert bins["near"] == 0, bins
+
+
 def test_deterministic_and_stream_safe():
     L, U, W, A = _random(13, 6, 5, 3000, 256)
     dU, dW = dev_factors(U, W)
