@@ -7,7 +7,9 @@
 // kernel computes it on bf16 MFMA (v_mfma_f32_32x32x16_bf16, fp32
 // accumulate) in 64-vocab tiles and consumes every logit in registers:
 //   z = L[row_p][v] + M[p][v]            (one fp32 add)
-//   running max / sum of 2^(z*log2e - c) per (lane, parent)  (log-sum-exp)
+//   sum of 2^(z*log2e - c) per (lane, parent)  (log-sum-exp; the tiled
+//   kernel fixes the shift c just below the parent's threshold, the thin
+//   form keeps a running maximum)
 //   candidates z >= theta_p kept in a per-(lane, parent) top-k list
 // The logit rows are never written back (unless z_out asks for them).
 //
@@ -177,7 +179,7 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
   bf16x8 uf[NB][R16];
   const float* lrow[NB];
   int lslot[NB];
-  float thr[NB], cm2[NB], ss[NB];
+  float thr[NB], cm2[NB], ss[NB], hb[NB];
   // per-parent scalars first: a wait for any of them (vmcnt counts in
   // order) then cannot hold up the fragment loads issued after them
   int ptk[NB];
@@ -196,8 +198,11 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
     lrow[b] = (!STAGED && has_L) ? a.L + row * a.lstride : nullptr;
     lslot[b] = STAGED ? pc / a.group_fp - g0 : 0;
     thr[b] = valid ? (a.theta ? a.theta[p] : neg_inf()) : pos_inf();
-    cm2[b] = neg_inf();
+    // the exponent shift of the lane's sum: fixed just below the threshold
+    // (+inf past the parents, whose sums stay 0)
+    cm2[b] = valid ? thr[b] * kLog2e - 1.f : pos_inf();
     ss[b] = 0.f;
+    hb[b] = 1.f;
   }
   // The fragment loads are unconditional and in bounds (a block past the
   // parents reads block 0; the packed buffer holds whole blocks), so that
@@ -383,10 +388,6 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
             z[j] = v < a.V ? l + acc[b][j] : neg_inf();
           }
         }
-        float m = z[0];
-#pragma unroll
-        for (int j = 1; j < 16; ++j) m = fmaxf(m, z[j]);
-
         const int p = pw + 32 * b + col;
         if (!STAGED && a.z_out != nullptr && p < a.P) {
 #pragma unroll
@@ -395,31 +396,49 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
             if (v < a.V) a.z_out[(int64_t)p * a.V + v] = z[j];
           }
         }
-        // online log-sum-exp in log2 units
-        const float m2 = m * kLog2e;
-        if (m2 > cm2[b]) {
-          ss[b] *= __builtin_amdgcn_exp2f(cm2[b] - m2);
-          cm2[b] = m2;
-        }
-        if (m != neg_inf()) {
-          float sg[4];
+        // log-sum-exp in log2 units with the fixed shift cm2: no running
+        // maximum.  An element at or above the threshold contributes at
+        // least 2^(thr*log2e - cm2) = 2 hb to the group's sum, so a group
+        // whose sum stays below hb holds no candidate (the test can only
+        // err towards the rare path).
+        float sg4[4];
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const float e0 = __builtin_amdgcn_exp2f(fmaf(z[4 * g], kLog2e, -cm2[b]));
-            const float e1 = __builtin_amdgcn_exp2f(fmaf(z[4 * g + 1], kLog2e, -cm2[b]));
-            const float e2 = __builtin_amdgcn_exp2f(fmaf(z[4 * g + 2], kLog2e, -cm2[b]));
-            const float e3 = __builtin_amdgcn_exp2f(fmaf(z[4 * g + 3], kLog2e, -cm2[b]));
-            sg[g] = (e0 + e1) + (e2 + e3);
-          }
-          ss[b] += (sg[0] + sg[1]) + (sg[2] + sg[3]);
+        for (int g = 0; g < 4; ++g) {
+          const float e0 = __builtin_amdgcn_exp2f(fmaf(z[4 * g], kLog2e, -cm2[b]));
+          const float e1 = __builtin_amdgcn_exp2f(fmaf(z[4 * g + 1], kLog2e, -cm2[b]));
+          const float e2 = __builtin_amdgcn_exp2f(fmaf(z[4 * g + 2], kLog2e, -cm2[b]));
+          const float e3 = __builtin_amdgcn_exp2f(fmaf(z[4 * g + 3], kLog2e, -cm2[b]));
+          sg4[g] = (e0 + e1) + (e2 + e3);
         }
-        // rare path: some element may enter this lane's top-k.  A rolled
-        // loop that shifts z keeps the code small; z is dead afterwards.
-        // The loop ends after the last element at or above the threshold
-        // (which only rises as the list fills).
-        const bool hit = m >= thr[b];
+        const float sg = (sg4[0] + sg4[1]) + (sg4[2] + sg4[3]);
+        const bool hit = !(sg < hb[b]);
+        if (!hit) ss[b] += sg;
+        // rare path: some element may enter this lane's top-k, or the sum
+        // needs another shift.  A rolled loop that shifts z keeps the code
+        // small; z is dead afterwards.  The loop ends after the last element
+        // at or above the threshold (which only rises as the list fills).
         if (__any(hit)) {
           if (hit) {
+            float m = z[0];
+#pragma unroll
+            for (int j = 1; j < 16; ++j) m = fmaxf(m, z[j]);
+            float s16 = sg;
+            if (m == neg_inf()) {
+              // nothing to add (under a shift of -inf the sum is NaN)
+              s16 = 0.f;
+            } else if (!(fmaf(m, kLog2e, -cm2[b]) <= 64.f)) {
+              // far above the shift (or the first finite group of a parent
+              // without a threshold): shift to this group's maximum
+              const float cn = m * kLog2e;
+              ss[b] = ss[b] == 0.f ? 0.f
+                                   : ss[b] * __builtin_amdgcn_exp2f(cm2[b] - cn);
+              cm2[b] = cn;
+              s16 = 0.f;
+#pragma unroll
+              for (int j = 0; j < 16; ++j)
+                s16 += __builtin_amdgcn_exp2f(fmaf(z[j], kLog2e, -cn));
+            }
+            ss[b] += s16;
             const int li = (wave * 64 + lane) * NB + b;
             ZV* lst = lists + li * a.k;
             int cnt = lcount[li];
@@ -437,6 +456,7 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
               v += ((j & 3) == 3) ? 5 : 1;
             }
             lcount[li] = cnt;
+            hb[b] = __builtin_amdgcn_exp2f(fmaf(thr[b], kLog2e, -cm2[b]) - 1.f);
           }
         }
       }
@@ -544,7 +564,7 @@ __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
 
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    float c2 = cm2[b], s = ss[b];
+    float c2 = ss[b] > 0.f ? cm2[b] : neg_inf(), s = ss[b];
     combine_halves(c2, s, lane);
     const int p = pw + 32 * b + col;
     if (p < a.P) {
