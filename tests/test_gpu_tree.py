@@ -220,6 +220,24 @@ def test_integer_ties_in_queued_tile_order():
     assert bins["near"] == 0, bins
 
 
+@pytest.mark.parametrize("batch,beam", [(32, 16), (12, 16)])
+def test_spiked_rows_move_the_exponent_shift(batch, beam):
+    # Some L rows hold one logit 60 or 120 above the rest (natural units):
+    # the fused kernel's exponent sum starts from a shift just below the
+    # seed threshold, and a group that lies more than 64 (log2 units) above
+    # it, up to past the fp32 range of 2^(z*log2e - shift), must move the
+    # shift.  32 requests give 512-parent launches (queued tiles), 12 give
+    # 192 (contiguous slices).
+    L, U, W, A = _random(41 + batch, batch, 4, 6000, 256)
+    rng = np.random.default_rng(43)
+    for q in range(batch):
+        for d in range(4):
+            if (q + d) % 3 == 0:
+                L[q, d, rng.integers(0, 6000)] += 60.0 if (q + d) % 2 else 120.0
+    g, o, bins = run_and_compare(L, U, W, A, 8, beam, 64)
+    assert bins["near"] <= 1, bins
+
+
 def test_deterministic_and_stream_safe():
     L, U, W, A = _random(13, 6, 5, 3000, 256)
     dU, dW = dev_factors(U, W)
