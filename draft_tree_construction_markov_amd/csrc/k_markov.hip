@@ -150,12 +150,17 @@ K1Plan plan_k1(int P, int V, int r, int k, int uw_dtype, bool has_uw,
     auto lists_of = [&](int nb, int nw) {  // lists + their lengths
       return (size_t)nw * 64 * nb * (k * sizeof(ZV) + sizeof(int));
     };
-    const size_t staged_l = (size_t)2 * kLdsRowSlots * 16 * 16;
     const size_t direct_l = (size_t)2 * 4 * 16 * 16;
+    // L bytes of a shape: two buffers of ls row slots of 256 bytes each
+    // (ls = 0: rows read directly)
+    auto l_bytes = [&](int ls) {
+      return ls > 0 ? (size_t)2 * ls * 16 * 16 : direct_l;
+    };
     // Eight waves (two per SIMD, so that one's epilogue overlaps the other's
     // MFMA chain) in this order of preference:
     //   64 parents per wave, L rows staged in LDS (more than 256 parents);
-    //   32 parents per wave, staged L rows;
+    //   32 parents per wave, staged L rows (36 slots, or 16 beside long
+    //   lists);
     //   32 parents per wave, L rows read directly (large k, or groups too
     //   small for the row slots).
     // Measured at 640 parents with k = 20: 105 us against 362 us for two
@@ -163,31 +168,31 @@ K1Plan plan_k1(int P, int V, int r, int k, int uw_dtype, bool has_uw,
     // 172 us for one-wave workgroups.  Waves past the parents only load
     // their share of each tile: with few parents the launch is bound by
     // the tile loads, and eight waves issue them faster than one.
-    auto fits = [&](int nb, bool staged) {
-      if (staged && (group_fp <= 0 || slots_of(nb, 8) > kLdsRowSlots))
-        return false;
-      return wbytes + (staged ? staged_l : direct_l) + lists_of(nb, 8) <=
-             kLdsPerCU;
+    auto fits = [&](int nb, int ls) {
+      if (ls > 0 && (group_fp <= 0 || slots_of(nb, 8) > ls)) return false;
+      return wbytes + l_bytes(ls) + lists_of(nb, 8) <= kLdsPerCU;
     };
-    auto take = [&](int nb, int nw, bool staged) {
+    auto take = [&](int nb, int nw, int ls) {
       pl.NB = nb;
       pl.NW = nw;
-      pl.lslots = staged ? kLdsRowSlots : 0;
+      pl.lslots = ls;
       pl.lds = lists_of(nb, nw);
-      pl.lds_total = wbytes + (staged ? staged_l : direct_l) + pl.lds;
+      pl.lds_total = wbytes + l_bytes(ls) + pl.lds;
     };
-    if (P > 256 && fits(2, true)) {
-      take(2, 8, true);
-    } else if (fits(1, true)) {
-      take(1, 8, true);
-    } else if (fits(1, false)) {
-      take(1, 8, false);
+    if (P > 256 && fits(2, kLdsRowSlots)) {
+      take(2, 8, kLdsRowSlots);
+    } else if (fits(1, kLdsRowSlots)) {
+      take(1, 8, kLdsRowSlots);
+    } else if (fits(1, kSmallRowSlots)) {
+      take(1, 8, kSmallRowSlots);
+    } else if (fits(1, 0)) {
+      take(1, 8, 0);
     } else {
       // very long lists: fewer waves of 64 parents, L rows read directly
       int nw = 4;
       while (nw > 1 && wbytes + direct_l + lists_of(2, nw) > kLdsPerCU)
         nw /= 2;
-      take(2, nw, false);
+      take(2, nw, 0);
     }
     int per_cu = (int)(kLdsPerCU / pl.lds_total);
     if (per_cu < 1) per_cu = 1;

@@ -123,13 +123,13 @@ __device__ __forceinline__ float quad_bcast(float x, int g) {
   return __builtin_bit_cast(float, r);
 }
 
-template <int NB, int NW, int R16, bool STAGED>
+template <int NB, int NW, int R16, bool STAGED, int LSL = kLdsRowSlots>
 __global__ __launch_bounds__(NW * 64) void markov_topk_mfma(K1Args a) {
   constexpr int CH = 2 * R16;               // 16-byte chunks per W row
   constexpr int RS = wstride<R16>();       // chunks per padded LDS row
   constexpr int TILE_CH = 64 * RS;          // chunk slots per 64-row tile
   constexpr int SPAN = NW * NB * 32;        // parents per workgroup
-  constexpr int LS = STAGED ? kLdsRowSlots : 4;
+  constexpr int LS = STAGED ? LSL : 4;  // L row slots per buffer
   // Double buffers as distinct LDS objects: the loop is unrolled by two so
   // that every read names one buffer and every direct global->LDS load the
   // other, which lets the compiler keep the next tile's loads in flight
@@ -762,9 +762,9 @@ hipError_t go_thin(const K1Plan& pl, const K1Args& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int NB, int NW, int R16, bool STAGED>
+template <int NB, int NW, int R16, bool STAGED, int LSL = kLdsRowSlots>
 hipError_t go_mfma(const K1Plan& pl, const K1Args& a, hipStream_t s) {
-  auto fn = markov_topk_mfma<NB, NW, R16, STAGED>;
+  auto fn = markov_topk_mfma<NB, NW, R16, STAGED, LSL>;
   hipError_t e = allow_lds(reinterpret_cast<const void*>(fn), pl.lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(fn, pl.grid, pl.block, pl.lds, s, a);
@@ -779,9 +779,13 @@ hipError_t launch_mfma_rank(const K1Plan& pl, const K1Args& a,
   if constexpr (!STAGED) {
     if (pl.thin) return go_thin<R16>(pl, a, s);
   }
-  if (pl.NB == 1)
-    return pl.NW == 8 ? go_mfma<1, 8, R16, STAGED>(pl, a, s)
-                      : go_mfma<1, 1, R16, STAGED>(pl, a, s);
+  if (pl.NB == 1) {
+    if (pl.NW != 8) return go_mfma<1, 1, R16, STAGED>(pl, a, s);
+    // long lists leave room for fewer staged L rows
+    if (STAGED && pl.lslots == kSmallRowSlots)
+      return go_mfma<1, 8, R16, STAGED, kSmallRowSlots>(pl, a, s);
+    return go_mfma<1, 8, R16, STAGED>(pl, a, s);
+  }
   switch (pl.NW) {
     case 8: return go_mfma<2, 8, R16, STAGED>(pl, a, s);
     case 4: return go_mfma<2, 4, R16, STAGED>(pl, a, s);

@@ -71,6 +71,7 @@ struct K1Plan {
 
 constexpr int kSeedT = 32;         // top tokens of each L row used for seeds
 constexpr int kLdsRowSlots = 36;   // staged L rows per buffer (fused kernel)
+constexpr int kSmallRowSlots = 16; // the same, beside long top-k lists
 constexpr int kSimpleThreads = 128;
 constexpr int kMaxPool = 8192;     // generated children per request
 constexpr int kMaxCand = 2048;     // children per request and depth
