@@ -29,6 +29,7 @@ namespace pct {
 // contributes the kSeedT / kRowTopPieces best of those.  Any subset is a
 // valid seed; this one is close to the row's top kSeedT.
 constexpr int kRowTopPieces = 8;
+constexpr int kRowTopVec = 19;  // 16-byte loads per thread and round
 constexpr int kRowTopSlots = kSeedT / kRowTopPieces;
 
 __global__ __launch_bounds__(256) void row_top_kernel(const float* L, int V,
@@ -59,21 +60,22 @@ __global__ __launch_bounds__(256) void row_top_kernel(const float* L, int V,
   if (vec_ok) {
     const float4* L4 = reinterpret_cast<const float4*>(Lr);
     const int i0b = v0 / 4, i1 = v1 / 4;  // whole vectors; V % 4 == 0 here
-    // eight independent 16-byte loads in flight per thread; out-of-range
-    // slots reload the first vector of the piece and are masked to -inf.
-    // Non-temporal: the rows are read once here, and the factor matrix W,
-    // which every depth reads again, stays in the caches.
-    for (int i0 = i0b + tid; i0 < i1; i0 += 8 * 256) {
-      float4 x[8];
+    // kRowTopVec independent 16-byte loads in flight per thread (a whole
+    // piece of a 151936-token row in one round); out-of-range slots reload
+    // the first vector of the piece and are masked to -inf.  Non-temporal:
+    // the rows are read once here, and the factor matrix W, which every
+    // depth reads again, stays in the caches.
+    for (int i0 = i0b + tid; i0 < i1; i0 += kRowTopVec * 256) {
+      float4 x[kRowTopVec];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < kRowTopVec; ++u) {
         const int i = i0 + u * 256;
         const f32x4 y = __builtin_nontemporal_load(
             reinterpret_cast<const f32x4*>(L4 + (i < i1 ? i : i0b)));
         x[u] = make_float4(y.x, y.y, y.z, y.w);
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < kRowTopVec; ++u) {
         const int i = i0 + u * 256;
         const bool in = i < i1;
         const int v = 4 * i;
