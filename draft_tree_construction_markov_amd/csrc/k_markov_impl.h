@@ -782,8 +782,10 @@ hipError_t launch_mfma_rank(const K1Plan& pl, const K1Args& a,
   if (pl.NB == 1) {
     if (pl.NW != 8) return go_mfma<1, 1, R16, STAGED>(pl, a, s);
     // long lists leave room for fewer staged L rows
-    if (STAGED && pl.lslots == kSmallRowSlots)
-      return go_mfma<1, 8, R16, STAGED, kSmallRowSlots>(pl, a, s);
+    if constexpr (STAGED) {
+      if (pl.lslots == kSmallRowSlots)
+        return go_mfma<1, 8, R16, STAGED, kSmallRowSlots>(pl, a, s);
+    }
     return go_mfma<1, 8, R16, STAGED>(pl, a, s);
   }
   switch (pl.NW) {
