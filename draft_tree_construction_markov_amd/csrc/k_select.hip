@@ -539,6 +539,10 @@ __global__ __launch_bounds__(kInitThreads) void init_kernel(
     for (int c = tid; c < ch; c += kInitThreads)
       sa.upack[upack_index(q, c, ch / 2)] = urow[c];
   }
+  // the fused kernel's tile queue starts the build cleared (every launch
+  // leaves it cleared)
+  if (q == 0)
+    for (int i = tid; i < n_tq; i += kInitThreads) tq[i] = 0;
   if (tid >= 64) return;
   if (!mf) th = seed_theta(sa, a, q * B, lane);
   if (lane == 0) {
@@ -549,10 +553,6 @@ __global__ __launch_bounds__(kInitThreads) void init_kernel(
     f.theta[q] = th;
     gcnt[q] = 0;
   }
-  // the fused kernel's tile queue starts the build cleared (every launch
-  // leaves it cleared)
-  if (q == 0)
-    for (int i = tid; i < n_tq; i += kInitThreads) tq[i] = 0;
 }
 
 // The log-normaliser of one parent from its (c, s) partials, one wave:

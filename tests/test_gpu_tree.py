@@ -238,6 +238,31 @@ def test_spiked_rows_move_the_exponent_shift(batch, beam):
     assert bins["near"] <= 1, bins
 
 
+def test_tile_queue_cleared_for_large_frontiers():
+    # 17600 parents at depth 3 make 35 parent tiles, so the fused kernel's
+    # tile queue has 70 counters; the build clears them itself, so a
+    # workspace full of stale bytes must give the same trees as a cleared one
+    batch, B, V, r = 1100, 3, 2000, 32
+    L, U, W, A = _random(53, batch, B, V, r)
+    dU, dW = dev_factors(U, W)
+    dL, dA = dev_f32(L), dev_i32(A)
+    announce("tile queue", dict(batch=batch, B=B, V=V))
+    tb = pct.TreeBuilder(batch, B, V, 8, 16, 16, r=r, mask=False)
+    tb.ws.fill_(0x41)
+    a = {k: v.clone() for k, v in vars(tb.run(dL, dU, dW, dA)).items()
+         if v is not None}
+    tb.ws.zero_()
+    b = tb.run(dL, dU, dW, dA)
+    for key in ("tok", "parent", "depth", "score", "n_nodes"):
+        assert torch.equal(a[key], getattr(b, key)), key
+    # and a few requests against the oracle
+    g = b.numpy()
+    reqs = [0, 549, 1099]
+    o = oracle.build_tree(L[reqs], U, W, A[reqs], 8, 16, 16)
+    bins = compare_all(g, o, L, U, W, A, 8, 16, 16, reqs, mask=False)
+    assert bins["exact"] == len(reqs), bins
+
+
 def test_deterministic_and_stream_safe():
     L, U, W, A = _random(13, 6, 5, 3000, 256)
     dU, dW = dev_factors(U, W)
