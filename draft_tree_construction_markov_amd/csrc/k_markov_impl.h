@@ -612,17 +612,24 @@ __global__ __launch_bounds__(kThinWaves * 64) void markov_topk_thin(
   row = row < 0 ? 0 : (row >= a.L_rows ? a.L_rows - 1 : row);
   const float* lrow = has_L ? a.L + row * a.lstride : nullptr;
   bf16x8 uf[R16];
+  // Rank step kk of lane half h takes the rank chunk R16*h + kk (a
+  // relabelling of the contraction index, the same for U and W), so that a
+  // lane's W loads walk a contiguous half row.
   if (a.upack != nullptr) {
-    const uint4* up = a.upack + lane;  // block 0, one 1 KB load per step
+    // block 0; chunk c of the packed rows sits at (c/2)*64 + (c%2)*32 + col
 #pragma unroll
-    for (int kk = 0; kk < R16; ++kk)
-      uf[kk] = __builtin_bit_cast(bf16x8, up[kk * 64]);
+    for (int kk = 0; kk < R16; ++kk) {
+      const int c = R16 * h + kk;
+      uf[kk] = __builtin_bit_cast(bf16x8,
+                                  a.upack[(c >> 1) * 64 + (c & 1) * 32 + col]);
+    }
   } else {
     const int ptk = min(max(a.ptok[pc], 0), a.V - 1);
-    const uint4* up = reinterpret_cast<const uint4*>(a.U) + (int64_t)ptk * CH + h;
+    const uint4* up =
+        reinterpret_cast<const uint4*>(a.U) + (int64_t)ptk * CH + R16 * h;
 #pragma unroll
     for (int kk = 0; kk < R16; ++kk)
-      uf[kk] = __builtin_bit_cast(bf16x8, up[2 * kk]);
+      uf[kk] = __builtin_bit_cast(bf16x8, up[kk]);
   }
   if (!valid) {
 #pragma unroll
@@ -635,12 +642,12 @@ __global__ __launch_bounds__(kThinWaves * 64) void markov_topk_thin(
   const uint4* Wg = reinterpret_cast<const uint4*>(a.W);
   for (int v0 = r0 + 32 * wave; v0 < r1; v0 += 32 * kThinWaves) {
     // W rows v0 + col (rows past V read row V - 1; their outputs are
-    // masked), chunks 2kk + h: the MFMA operand of rank step kk
-    const uint4* wp = Wg + (int64_t)min(v0 + col, a.V - 1) * CH + h;
+    // masked), chunks R16*h + kk: the MFMA operand of rank step kk
+    const uint4* wp = Wg + (int64_t)min(v0 + col, a.V - 1) * CH + R16 * h;
     bf16x8 wf[R16];
 #pragma unroll
     for (int kk = 0; kk < R16; ++kk)
-      wf[kk] = __builtin_bit_cast(bf16x8, wp[2 * kk]);
+      wf[kk] = __builtin_bit_cast(bf16x8, wp[kk]);
     // register j of this lane holds vocab vb + 8*(j/4) + j%4
     const int vb = v0 + 4 * h;
     const bool full = v0 + 32 <= a.V;
