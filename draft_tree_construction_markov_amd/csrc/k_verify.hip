@@ -61,32 +61,63 @@ __global__ __launch_bounds__(64) void accept_kernel(
   const int words = (N + 63) / 64;
   uint64_t* mbits = reinterpret_cast<uint64_t*>(smem);
   int32_t* par = reinterpret_cast<int32_t*>(mbits + words);
-  uint8_t* ok = reinterpret_cast<uint8_t*>(par + N);
+  int32_t* ts = par + N;
+  uint8_t* ok = reinterpret_cast<uint8_t*>(ts + N);
   const int q = blockIdx.x, lane = threadIdx.x;
   const int n = min(n_nodes[q], N);
   const int32_t* T = tok + (int64_t)q * N;
   const int32_t* Pa = parent + (int64_t)q * N;
   const int32_t* D = depth + (int64_t)q * N;
   const int32_t* tg = target + (int64_t)q * (N + 1);
-  // match bits, one word per 64 nodes (a whole wave per word)
-  for (int w = 0; w < words; ++w) {
-    const int i = 64 * w + lane;
-    bool m = false;
-    if (i < n) {
-      const int p = Pa[i];
-      par[i] = p;
-      m = (p >= -1 && p < i) && T[i] == tg[p + 1];
-      ok[i] = m;
+  // match bits, one word per 64 nodes (a whole wave per word); the loads of
+  // kAccW words are in flight together (parents and tokens, then the
+  // target tokens after the parents)
+  constexpr int kAccW = 8;
+  for (int w0 = 0; w0 < words; w0 += kAccW) {
+    int p[kAccW], tk[kAccW], tt[kAccW];
+#pragma unroll
+    for (int u = 0; u < kAccW; ++u) {
+      const int i = 64 * (w0 + u) + lane;
+      const bool in = w0 + u < words && i < n;
+      p[u] = in ? Pa[i] : -2;
+      tk[u] = in ? T[i] : 0;
     }
-    const uint64_t b = __ballot(m);
-    if (lane == 0) mbits[w] = b;
+#pragma unroll
+    for (int u = 0; u < kAccW; ++u) {
+      const int i = 64 * (w0 + u) + lane;
+      tt[u] = (p[u] >= -1 && p[u] < i) ? tg[p[u] + 1] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kAccW; ++u) {
+      if (w0 + u >= words) break;
+      const int i = 64 * (w0 + u) + lane;
+      bool m = false;
+      if (i < n) {
+        m = (p[u] >= -1 && p[u] < i) && tk[u] == tt[u];
+        par[i] = p[u];
+        ts[i] = tk[u];
+        ok[i] = m;
+      }
+      const uint64_t b = __ballot(m);
+      if (lane == 0) mbits[w0 + u] = b;
+    }
   }
   __syncthreads();
   // deepest accepted node: key = depth * 2^20 + (2^20 - 1 - i)
   int best = -1;
   for (int i = lane; i < n; i += kWave) {
     bool acc = true;
-    if (mask != nullptr) {
+    if (mask != nullptr && words <= kAccW) {
+      // the node's whole mask row in flight at once
+      const uint64_t* row = mask + ((int64_t)q * N + i) * words;
+      uint64_t r[kAccW];
+#pragma unroll
+      for (int w = 0; w < kAccW; ++w) r[w] = w < words ? row[w] : 0;
+#pragma unroll
+      for (int w = 0; w < kAccW; ++w)
+        acc = acc && (w >= words || (r[w] & ~mbits[w]) == 0);
+      acc = acc && ok[i];
+    } else if (mask != nullptr) {
       const uint64_t* row = mask + ((int64_t)q * N + i) * words;
       for (int w = 0; w < words && acc; ++w) acc = (row[w] & ~mbits[w]) == 0;
       acc = acc && ok[i];
@@ -123,7 +154,7 @@ __global__ __launch_bounds__(64) void accept_kernel(
       for (int j = dl - 1; j >= 0 && a >= 0; --j) {
         if (j < B) {
           an[j] = a;
-          at[j] = T[a];
+          at[j] = ts[a];
         }
         a = par[a];
       }
@@ -306,7 +337,9 @@ hipError_t launch_accept(int batch, int N, int B, const int32_t* tok,
                          const int32_t* target, int32_t* tau,
                          int32_t* accept_node, int32_t* accept_tok,
                          hipStream_t s) {
-  const size_t lds = (size_t)(N + 63) / 64 * 8 + (size_t)N * 5;
+  const size_t lds = (size_t)(N + 63) / 64 * 8 + (size_t)N * 9;
+  hipError_t e = allow_lds(reinterpret_cast<const void*>(accept_kernel), lds);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(accept_kernel, dim3(batch), dim3(64), lds, s, N, B, tok,
                      parent, depth, n_nodes, mask, target, tau, accept_node,
                      accept_tok);
