@@ -443,6 +443,53 @@ def test_verify_worked_example():
     assert at[0].cpu().tolist() == g["expected_accept_tok"]
 
 
+def _random_tree(rng, N, n, B):
+    """Parents before children, depth <= B, siblings numbered 0, 1, ... as
+    their tokens (so siblings never share a token)."""
+    par = np.full(N, -1, np.int32)
+    dep = np.zeros(N, np.int32)
+    tok = np.zeros(N, np.int32)
+    kids = {}
+    for i in range(n):
+        p = -1
+        if i > 0 and rng.random() > 0.02:
+            p = int(rng.integers(max(0, i - 64), i))
+            if dep[p] >= B:
+                p = -1
+        par[i] = p
+        dep[i] = 1 if p < 0 else dep[p] + 1
+        tok[i] = kids.get(p, 0)
+        kids[p] = tok[i] + 1
+    return tok, par, dep
+
+
+@pytest.mark.parametrize("N,ns", [(8192, (8192, 5000)), (700, (700, 321))])
+def test_walk_on_large_trees(N, ns):
+    # N = 8192, the largest the call takes (128 mask words per node, more
+    # than 64 KB of LDS), and N = 700 (11 words): the acceptance test's
+    # word-by-word path, with and without the mask
+    rng = np.random.default_rng(N + 61)
+    B = 12
+    trees = [_random_tree(rng, N, n, B) for n in ns]
+    tok = np.stack([x[0] for x in trees])
+    par = np.stack([x[1] for x in trees])
+    dep = np.stack([x[2] for x in trees])
+    n = np.array(ns, np.int32)
+    tgt = rng.integers(0, 3, size=(len(ns), N + 1)).astype(np.int32)
+    announce("walk large", dict(N=N))
+    args = (dev_i32(tok), dev_i32(par), dev_i32(dep), dev_i32(n), dev_i32(tgt),
+            B)
+    mk = pct.tree_mask(dev_i32(par), dev_i32(n))
+    for m in (None, mk):
+        tau, an, at = pct.verify_accept(*args, mask=m)
+        tau, an, at = (x.cpu().numpy() for x in (tau, an, at))
+        for q in range(len(ns)):
+            t2, an2, at2 = oracle.accept(tok[q], par[q], int(n[q]), B, tgt[q])
+            assert int(tau[q]) == t2, (q, m is None)
+            assert list(an[q]) == list(an2), q
+            assert list(at[q]) == list(at2), q
+
+
 def test_mask_edge_cases():
     announce("mask edges")
     N = 130
