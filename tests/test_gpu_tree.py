@@ -202,6 +202,15 @@ def test_chain_and_uniform_ties():
     assert bins["exact"] == 2
 
 
+def test_long_lists_small_staged_form_without_quads():
+    # k = 20 leaves LDS for 16 staged L row slots only; beam 18 makes groups
+    # of 18 parents (not whole quads of lanes), so the staged form reads each
+    # lane's L values itself; 360 parents per depth, ragged last tile
+    L, U, W, A = _random(71, 20, 3, 5000, 256)
+    g, o, bins = run_and_compare(L, U, W, A, 20, 18, 100)
+    assert bins["near"] <= 1, bins
+
+
 def test_integer_ties_in_queued_tile_order():
     # Integer factors and logits: every z = L + U.W is an exact integer, so
     # children of one parent tie exactly, also at the top-k boundary.  Depth
