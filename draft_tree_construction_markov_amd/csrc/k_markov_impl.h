@@ -18,8 +18,8 @@
 // 32x32 output block and 16 vocab rows of it: per-parent state lives in a
 // handful of registers.  Each wave keeps the U rows of its 64 (NB=2) or 32
 // (NB=1) parents resident in registers for the whole kernel; the W tile is
-// staged through LDS by direct global->LDS loads (double-buffered,
-// XOR-swizzled 16-byte chunks) and shared by all waves of the workgroup;
+// staged through LDS by direct global->LDS loads (double-buffered, rows
+// padded by one 16-byte chunk) and shared by all waves of the workgroup;
 // so are the workgroup's L rows when parents are grouped by request.  A
 // workgroup covers a slice of the vocabulary for up to NB*NW*32 parents;
 // slices x parent tiles form the grid.  With 64 parents per wave a slice is
