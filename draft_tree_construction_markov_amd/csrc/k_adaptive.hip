@@ -903,6 +903,9 @@ __global__ __launch_bounds__(kBfThreads) void bestfirst_batched_kernel(
       const int npar = d == 1 ? 1 : le - lb;
       if (npar == 0) break;
       const float* row = lp + (d - 1) * kBfMaxK;
+      // the level's list, one entry per lane (Kl <= 64): block ends come
+      // from it by readlane, large families are written from it
+      const float rl = row[lane];
       int base = n_e;
       for (int x0 = 0; x0 < npar; x0 += kWave) {
         const int x = x0 + lane;
@@ -922,7 +925,12 @@ __global__ __launch_bounds__(kBfThreads) void bestfirst_batched_kernel(
           };
           int b = 0;
 #pragma unroll
-          for (int k = 0; k < 8; ++k) b += pass(row[8 * k + 7]) ? 1 : 0;
+          for (int k = 0; k < 8; ++k)
+            b += pass(__builtin_bit_cast(
+                     float, __builtin_amdgcn_readlane(
+                                __builtin_bit_cast(int, rl), 8 * k + 7)))
+                     ? 1
+                     : 0;
           c = 8 * b;
           if (b < 8) {
 #pragma unroll
@@ -966,7 +974,7 @@ __global__ __launch_bounds__(kBfThreads) void bestfirst_batched_kernel(
           const int rL = __builtin_amdgcn_readlane(par, L);
           const float sL = __builtin_bit_cast(
               float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sx), L));
-          for (int j = lane; j < cL; j += kWave) put(pL + j, sL, row[j], rL, j);
+          if (lane < cL) put(pL + lane, sL, rl, rL, lane);  // cL <= Kl <= 64
         }
         base += tot;
       }
