@@ -840,10 +840,11 @@ __global__ __launch_bounds__(kBfThreads) void bestfirst_batched_kernel(
     BestFirstArgs a) {
   __shared__ float lp[kBfMaxRows * kBfMaxK];       // later: T's scores
   __shared__ uint32_t keys[kBfMaxRows * kBfMaxK];  // later: T, its ranks
-  __shared__ float es[kBfCap];
-  __shared__ int16_t epar[kBfCap];
-  __shared__ uint8_t erank[kBfCap];
-  __shared__ uint8_t edep[kBfCap];
+  // prefixes; entries kBfCap + lane are wave 0's spare slots (below)
+  __shared__ float es[kBfCap + kWave];
+  __shared__ int16_t epar[kBfCap + kWave];
+  __shared__ uint8_t erank[kBfCap + kWave];
+  __shared__ uint8_t edep[kBfCap + kWave];
   __shared__ int16_t eout[kBfCap];
   __shared__ float ch[kBfMaxRows + 1];
   __shared__ int hist[512];
@@ -958,13 +959,13 @@ __global__ __launch_bounds__(kBfThreads) void bestfirst_batched_kernel(
           edep[pos] = (uint8_t)d;
         };
         // small families: each lane writes its own children from the block
-        // entries it holds; large ones (the chain node of a flat row has up
-        // to 64): the whole wave writes one family at a time
-        if (c <= 4) {
+        // entries it holds (block 0: c <= 4 means b == 0), four writes with
+        // no branch, those past the family into the lane's spare slot;
+        // large ones (the chain node of a flat row has up to 64): the whole
+        // wave writes one family at a time
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (j < c) put(pos0 + j, sx, blk[j], par, j);
-        }
+        for (int j = 0; j < 4; ++j)
+          put(c <= 4 && j < c ? pos0 + j : kBfCap + lane, sx, blk[j], par, j);
         uint64_t big = __ballot(c > 4);
         while (big) {
           const int L = __builtin_ctzll(big);
