@@ -913,9 +913,6 @@ __global__ __launch_bounds__(kBfThreads) void bestfirst_batched_kernel(
         const bool has = x < npar;
         const float sx = !has ? 0.0f : (d == 1 ? 0.0f : es[lb + x]);
         int c = 0;
-        float blk[7];  // entries of the located block (block 0 when c < 8)
-#pragma unroll
-        for (int i = 0; i < 7; ++i) blk[i] = 0.0f;
         if (has) {
           // qualifying children are a prefix of the sorted row: the last
           // entries of its 8-entry blocks locate the block, then the block
@@ -935,10 +932,7 @@ __global__ __launch_bounds__(kBfThreads) void bestfirst_batched_kernel(
           c = 8 * b;
           if (b < 8) {
 #pragma unroll
-            for (int i = 0; i < 7; ++i) {
-              blk[i] = row[8 * b + i];
-              c += pass(blk[i]) ? 1 : 0;
-            }
+            for (int i = 0; i < 7; ++i) c += pass(row[8 * b + i]) ? 1 : 0;
           }
           c = min(c, Kl);
         }
@@ -958,14 +952,18 @@ __global__ __launch_bounds__(kBfThreads) void bestfirst_batched_kernel(
           erank[pos] = (uint8_t)j;
           edep[pos] = (uint8_t)d;
         };
-        // small families: each lane writes its own children from the block
-        // entries it holds (block 0: c <= 4 means b == 0), four writes with
-        // no branch, those past the family into the lane's spare slot;
-        // large ones (the chain node of a flat row has up to 64): the whole
-        // wave writes one family at a time
+        // small families: each lane writes its own children, the level's
+        // first four list entries (the same for every lane; also when every
+        // block end passes, as with theta = -inf over a list of at most 4
+        // entries), four writes with no branch, those past the family into
+        // the lane's spare slot; large ones (the chain node of a flat row
+        // has up to 64): the whole wave writes one family at a time
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          put(c <= 4 && j < c ? pos0 + j : kBfCap + lane, sx, blk[j], par, j);
+          put(c <= 4 && j < c ? pos0 + j : kBfCap + lane, sx,
+              __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                            __builtin_bit_cast(int, rl), j)),
+              par, j);
         uint64_t big = __ballot(c > 4);
         while (big) {
           const int L = __builtin_ctzll(big);
