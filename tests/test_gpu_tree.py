@@ -102,6 +102,16 @@ def test_markov_tree_parity(batch, B, V, k, beam, N, r):
     run_and_compare(L, U, W, A, k, beam, N)
 
 
+@pytest.mark.parametrize("batch,B,V,k,beam,N,r", [
+    (3, 3, 40, 4, 6, 30, 64),    # the whole vocabulary in one ragged tile
+    (2, 4, 20, 8, 12, 50, 32),   # fewer tokens than the 32 seed slots
+    (2, 2, 5, 5, 10, 30, 32),    # k = V: every token of every parent
+])
+def test_vocab_smaller_than_a_tile(batch, B, V, k, beam, N, r):
+    L, U, W, A = _random(batch * 17 + V, batch, B, V, r)
+    run_and_compare(L, U, W, A, k, beam, N)
+
+
 @pytest.mark.parametrize("batch,B,V,k,beam,N,r,reqs", [
     # frontiers above 256 parents take the 8-wave fused kernel (512
     # parents per workgroup): 576-640 parents make two parent tiles, the
