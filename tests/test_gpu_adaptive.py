@@ -152,12 +152,12 @@ def test_exhausted_tree_and_small_vocab():
     assert all(int(x) == 5 + 25 + 125 for x in g["n_star"])
 
 
-@pytest.mark.parametrize("V,B", [(2, 5), (3, 3), (4, 2)])
+@pytest.mark.parametrize("V,B", [(2, 5), (3, 3), (4, 2), (6, 2)])
 def test_full_tree_over_tiny_vocab_in_the_batched_pass(V, B):
     # the budget is the whole tree (at most 64 nodes, so the batched pass
     # takes it) and exceeds the B*V single deviations, so the threshold is
     # -inf and every block end of the padded lists passes; every family has
-    # at most 4 children
+    # at most 4 children, or 6 (written by the whole wave)
     rng = np.random.default_rng(11 + V)
     L = (rng.normal(size=(4, B, V)) * 2.0).astype(np.float32)
     ctx = np.array([100, 2000, 9000, 30000], np.int32)
