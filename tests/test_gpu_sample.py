@@ -19,6 +19,7 @@ pytestmark = pytest.mark.gpu
     (6, 5, 3000, 4, 8, 48, 0.7, 1),
     (4, 4, 2049, 8, 16, 100, 1.5, 2),    # ragged vocabulary
     (3, 3, 64, 3, 9, 30, 0.05, 3),       # near-greedy temperature
+    (2, 3, 5, 3, 6, 20, 1.0, 4),         # five tokens: one short slice
 ])
 def test_sampled_targets_and_walk(batch, B, V, k, beam, N, T, seed):
     rng = np.random.default_rng(seed)
